@@ -1,0 +1,193 @@
+"""Exact attention forward on MI355X (gfx950): Python binding of libattn.so.
+
+The binding only marshals arguments: it checks tensor shapes, dtypes and
+devices, takes device pointers and the current HIP stream from PyTorch, and
+calls the C ABI declared in ``include/attn.h``. Every step of the attention
+computation runs in the HIP kernels of ``libattn.so``; there is no fallback
+path, and a missing library raises instead of computing anything elsewhere.
+
+Functions (same names as the C ABI):
+
+``attn_fwd(q, k, v, o, lse, causal=False, alpha=None, stream=None)``
+    16-bit (bf16 / f16) forward; q, k, v, o are [B, N, H, d] tensors, lse is
+    float32 [B, H, N].
+``attn_fp8_prepare(x, x8, descale, block_rows=128, hadamard=False, seed=0, stream=None)``
+    Hadamard transform (optional) + block quantisation of a bf16 tensor to
+    e4m3 codes (uint8) and float32 descales.
+``attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False,
+alpha=None, block_rows=128, stream=None)``
+    Forward on e4m3 inputs with a bf16 output.
+``attn_last_error()``
+    Message of the last failed call on this thread.
+
+Convenience wrappers that allocate the outputs with torch: ``attention`` and
+``fp8_prepare``/``attention_fp8``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8",
+    "attn_last_error", "attention", "fp8_prepare", "attention_fp8", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
+DTYPE_BF16, DTYPE_F16 = 0, 1
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_last_error", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"attn status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libattn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is missing: build it with "
+                           "`python -m exact_attention_forward_attn_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fp8_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, i, ctypes.c_uint64, vp]
+    lib.attn_fp8_prepare.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, i, vp]
+    lib.attn_fwd_fp8.restype = i
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def _check(status):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _default_alpha(d, alpha):
+    return 1.0 / math.sqrt(d) if alpha is None else float(alpha)
+
+
+def attn_fwd(q, k, v, o, lse, causal=False, alpha=None, stream=None):
+    """O = softmax(alpha q k^T) v and LSE for [B, N, H, d] bf16/f16 tensors."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, d]")
+    B, N, H, d = q.shape
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    for t, n in ((k, "k"), (v, "v"), (o, "o")):
+        _require(t, n, q.dtype, q.shape, q.device)
+    _require(q, "q", q.dtype, q.shape, q.device)
+    _require(lse, "lse", torch.float32, (B, H, N), q.device)
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
+                        _default_alpha(d, alpha), dt, _stream_handle(stream)))
+    return o, lse
+
+
+def attn_fp8_prepare(x, x8, descale, block_rows=128, hadamard=False, seed=0, stream=None):
+    """Block quantisation (and optional Hadamard transform) of bf16 x to e4m3."""
+    torch = _torch()
+    lib = load()
+    B, N, H, d = x.shape
+    _require(x, "x", torch.bfloat16, x.shape, x.device)
+    _require(x8, "x8", torch.uint8, x.shape, x.device)
+    nd = (B, H, (N + block_rows - 1) // block_rows) if block_rows else (1,)
+    _require(descale, "descale", torch.float32, nd, x.device)
+    _check(lib.attn_fp8_prepare(_ptr(x), _ptr(x8), _ptr(descale), B, H, N, d, int(block_rows),
+                                int(bool(hadamard)), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
+                                _stream_handle(stream)))
+    return x8, descale
+
+
+def attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False, alpha=None,
+                 block_rows=128, stream=None):
+    """Forward on e4m3 codes from attn_fp8_prepare; o is bf16."""
+    torch = _torch()
+    lib = load()
+    B, N, H, d = q8.shape
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _require(t, n, torch.uint8, q8.shape, q8.device)
+    _require(o, "o", torch.bfloat16, q8.shape, q8.device)
+    _require(lse, "lse", torch.float32, (B, H, N), q8.device)
+    nd = (B, H, (N + block_rows - 1) // block_rows) if block_rows else (1,)
+    for t, n in ((descale_q, "descale_q"), (descale_k, "descale_k"), (descale_v, "descale_v")):
+        _require(t, n, torch.float32, nd, q8.device)
+    _check(lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, H, N, d,
+                            int(bool(causal)), _default_alpha(d, alpha), _ptr(descale_q), _ptr(descale_k),
+                            _ptr(descale_v), int(block_rows), _stream_handle(stream)))
+    return o, lse
+
+
+def attention(q, k, v, causal=False, alpha=None, stream=None):
+    """Allocate O and LSE with torch and run attn_fwd."""
+    torch = _torch()
+    B, N, H, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    return attn_fwd(q, k, v, o, lse, causal, alpha, stream)
+
+
+def fp8_prepare(x, block_rows=128, hadamard=False, seed=0, stream=None):
+    torch = _torch()
+    B, N, H, d = x.shape
+    x8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    nd = (B, H, (N + block_rows - 1) // block_rows) if block_rows else (1,)
+    descale = torch.empty(nd, dtype=torch.float32, device=x.device)
+    return attn_fp8_prepare(x, x8, descale, block_rows, hadamard, seed, stream)
+
+
+def attention_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, alpha=None, block_rows=128,
+                  stream=None):
+    torch = _torch()
+    B, N, H, d = q8.shape
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    return attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, alpha, block_rows, stream)

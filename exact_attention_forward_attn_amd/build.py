@@ -1,0 +1,87 @@
+"""Builds libattn.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+``python -m exact_attention_forward_attn_amd.build`` compiles every source in
+``csrc/`` into ``exact_attention_forward_attn_amd/libattn.so``. The build
+always recompiles; nothing is cached.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libattn.so")
+ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fp8.hip"]
+
+COMMON = [
+    "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+# packed fp32 VALU forms are kept out of the generated code
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-munsafe-fp-atomics",
+             # MFMA accumulators in VGPRs: the softmax reads every score, and
+             # AGPR-resident scores would need a copy per element
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
+def _hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(args):
+    cmd, src = args
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in p.stdout.splitlines() if "packed-fp32-ops" not in l)
+    return src, p.returncode, out
+
+
+def build(verbose: bool = False, out: str = LIB) -> str:
+    hipcc = _hipcc()
+    tmp = tempfile.mkdtemp(prefix="attn_build_")
+    try:
+        jobs = []
+        objs = []
+        for src in SOURCES:
+            path = os.path.join(CSRC, src)
+            obj = os.path.join(tmp, src + ".o")
+            objs.append(obj)
+            if src.endswith(".hip"):
+                cmd = [hipcc, *HIP_FLAGS, *COMMON, "-c", path, "-o", obj]
+            else:
+                cmd = [hipcc, *COMMON, "-x", "c++", "-c", path, "-o", obj]
+            jobs.append((cmd, src))
+        with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+            results = list(ex.map(_compile, jobs))
+        failed = [r for r in results if r[1] != 0]
+        for src, rc, txt in results:
+            if verbose or rc != 0:
+                if txt.strip():
+                    print(f"[{src}]\n{txt}", file=sys.stderr)
+        if failed:
+            raise RuntimeError("compilation failed: " + ", ".join(r[0] for r in failed))
+        tmp_lib = out + ".tmp"
+        link = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        p = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if p.returncode != 0:
+            raise RuntimeError("link failed:\n" + p.stdout)
+        os.replace(tmp_lib, out)
+        return out
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,176 @@
+// C ABI front end of libattn.so (declared in include/attn.h).
+//
+// Every entry point validates its arguments on the host, before anything is
+// launched, and reports failures through a negative status plus a
+// thread-local message (attn_last_error). No exception crosses the ABI and
+// nothing is printed. The kernels live in the .hip translation units; this
+// file has no HIP dependency so its checks can be exercised without a GPU.
+
+#include "attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "attn_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Shape checks shared by the forward entry points. Returns ATTN_OK, a
+// negative status, or 1 for "valid but empty" (nothing to do).
+int check_shape(int B, int H, int N, int d, int elem_bytes) {
+  if (B < 0 || H < 0 || N < 0) return fail(ATTN_ERR_INVALID_ARG, "B, H, N must be >= 0 (got %d, %d, %d)", B, H, N);
+  if (d != 64 && d != 128 && d != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d is not supported (64, 128 or 256)", d);
+  if (B == 0 || H == 0 || N == 0) return 1;
+  // the kernels address one head with 32-bit byte offsets and index rows
+  // and LSE entries with 32-bit integers
+  const int64_t head_span = (int64_t)(N - 1) * H * d * elem_bytes + (int64_t)d * elem_bytes;
+  if (head_span >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "N*H*d too large for one batch entry (%lld bytes >= 2^31)",
+                (long long)head_span);
+  if ((int64_t)B * H * N >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "B*H*N too large (>= 2^31)");
+  return ATTN_OK;
+}
+
+int check_fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                     int N, int d, int causal, float alpha, int elem_bytes) {
+  const int s = check_shape(B, H, N, d, elem_bytes);
+  if (s != ATTN_OK) return s;
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!std::isfinite(alpha) || alpha < 0.f)
+    return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
+  const void* ptrs[5] = {q, k, v, o, lse};
+  const char* names[5] = {"q", "k", "v", "o", "lse"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  const int64_t in_bytes = (int64_t)B * N * H * d * elem_bytes;
+  const int64_t out_bytes = (int64_t)B * N * H * d * 2;
+  const int64_t lse_bytes = (int64_t)B * H * N * 4;
+  const void* ins[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, out_bytes, ins[i], in_bytes)) return fail(ATTN_ERR_INVALID_ARG, "o overlaps %s", names[i]);
+    if (overlaps(lse, lse_bytes, ins[i], in_bytes)) return fail(ATTN_ERR_INVALID_ARG, "lse overlaps %s", names[i]);
+  }
+  if (overlaps(o, out_bytes, lse, lse_bytes)) return fail(ATTN_ERR_INVALID_ARG, "o overlaps lse");
+  return ATTN_OK;
+}
+
+float scale_log2(float alpha) {
+  // alpha * log2(e); a zero scale is replaced by 1e-30, which gives the same
+  // float32 result (every exponent rounds to 2^0) and keeps the running max
+  // arithmetic free of 0 * inf.
+  const float c = alpha * 1.4426950408889634f;
+  return c < 1e-30f ? 1e-30f : c;
+}
+
+int hip_status(int err, const char* what) {
+  if (err == 0) return ok();
+  return fail(ATTN_ERR_HIP, "%s: HIP error %d (%s)", what, err, attn::hip_error_name(err));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             int causal, float alpha, int dtype, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
+  const int s = check_fwd_common(q, k, v, o, lse, B, H, N, d, causal, alpha, 2);
+  if (s == 1) return ok();
+  if (s != ATTN_OK) return s;
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal;
+  a.dtype = dtype;
+  a.scale_log2 = scale_log2(alpha);
+  return hip_status(attn::launch_fwd_16(a, stream), "attn_fwd launch");
+}
+
+int attn_fp8_prepare(const void* x, void* x8, float* descale, int B, int H, int N, int d, int block_rows,
+                     int hadamard, uint64_t hadamard_seed, void* stream) {
+  const int s = check_shape(B, H, N, d, 2);
+  if (s == 1) return ok();
+  if (s != ATTN_OK) return s;
+  if (block_rows != 0 && block_rows != 128)
+    return fail(ATTN_ERR_INVALID_ARG, "block_rows must be 0 or 128 (got %d)", block_rows);
+  if (hadamard != 0 && hadamard != 1) return fail(ATTN_ERR_INVALID_ARG, "hadamard must be 0 or 1");
+  const void* ptrs[3] = {x, x8, descale};
+  const char* names[3] = {"x", "x8", "descale"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  const int64_t n = (int64_t)B * N * H * d;
+  const int64_t dbytes = block_rows ? (int64_t)B * H * ((N + block_rows - 1) / block_rows) * 4 : 4;
+  if (overlaps(x8, n, x, 2 * n)) return fail(ATTN_ERR_INVALID_ARG, "x8 overlaps x");
+  if (overlaps(descale, dbytes, x, 2 * n)) return fail(ATTN_ERR_INVALID_ARG, "descale overlaps x");
+  if (overlaps(descale, dbytes, x8, n)) return fail(ATTN_ERR_INVALID_ARG, "descale overlaps x8");
+  attn::PrepArgs a{};
+  a.x = x; a.x8 = x8; a.descale = descale;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.block_rows = block_rows;
+  a.hadamard = hadamard;
+  a.seed = hadamard_seed;
+  return hip_status(attn::launch_fp8_prepare(a, stream), "attn_fp8_prepare launch");
+}
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse, int B, int H, int N,
+                 int d, int causal, float alpha, const float* descale_q, const float* descale_k,
+                 const float* descale_v, int block_rows, void* stream) {
+  const int s = check_fwd_common(q8, k8, v8, o, lse, B, H, N, d, causal, alpha, 1);
+  if (s == 1) return ok();
+  if (s != ATTN_OK) return s;
+  if (block_rows != 0 && block_rows != 128)
+    return fail(ATTN_ERR_INVALID_ARG, "block_rows must be 0 or 128 (got %d)", block_rows);
+  const float* ds[3] = {descale_q, descale_k, descale_v};
+  const char* names[3] = {"descale_q", "descale_k", "descale_v"};
+  for (int i = 0; i < 3; ++i)
+    if (!ds[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+  attn::FwdArgs a{};
+  a.q = q8; a.k = k8; a.v = v8; a.o = o; a.lse = lse;
+  a.dq = descale_q; a.dk = descale_k; a.dv = descale_v;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal;
+  a.block_rows = block_rows;
+  a.scale_log2 = scale_log2(alpha);
+  return hip_status(attn::launch_fwd_fp8(a, stream), "attn_fwd_fp8 launch");
+}
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+const char* attn_version(void) { return "attn-gfx950 0.1"; }
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal interface between the C ABI front end (attn_api.cpp) and the HIP
+// kernels. Not installed; the public ABI is include/attn.h.
+#pragma once
+
+#include <stdint.h>
+
+namespace attn {
+
+// Arguments of one attention forward launch, already validated on the host.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* dq;  // FP8 descales (null for 16-bit inputs)
+  const float* dk;
+  const float* dv;
+  int B, H, N, d;
+  int causal;
+  int dtype;       // 0 bf16, 1 f16 (16-bit path)
+  int block_rows;  // FP8: 128 or 0 (per tensor)
+  float scale_log2;  // alpha * log2(e), clamped to >= 1e-30
+};
+
+struct PrepArgs {
+  const void* x;
+  void* x8;
+  float* descale;
+  int B, H, N, d;
+  int block_rows;
+  int hadamard;
+  uint64_t seed;
+};
+
+// Each returns 0 on success or a hipError_t value.
+int launch_fwd_16(const FwdArgs& a, void* stream);
+int launch_fwd_fp8(const FwdArgs& a, void* stream);
+int launch_fp8_prepare(const PrepArgs& a, void* stream);
+const char* hip_error_name(int err);
+
+}  // namespace attn

@@ -1,0 +1,145 @@
+/*
+ * attn.h -- C ABI of the exact attention forward library (libattn.so).
+ *
+ * The library computes the exact attention forward pass
+ *     S = alpha * Q K^T,  P = softmax(S) (row-wise),  O = P V
+ * together with the per-row log-sum-exp LSE_i = ln sum_j exp(S_ij),
+ * without ever writing the N x N matrices S or P to device memory: each
+ * workgroup keeps one block of query rows on chip and streams blocks of K
+ * and V through it with the online (running max m, running sum l,
+ * unnormalised output O~) softmax recurrence.
+ *
+ * Passages defining the operations (pages on FlashAttention-3):
+ *   - "FlashAttention-3 paper review" (diycv.top), problem background:
+ *     S = alpha Q K^T, P = softmax(S), O = P V, alpha typically 1/sqrt(d).
+ *   - "FlashAttention-3 on Hopper", section 3.1 (masks as -inf before the
+ *     softmax), 3.2 and 4.2 (the online state and its invariant),
+ *     4.6 (finalize: empty rows give O = 0 and LSE = -inf; LSE in natural-log
+ *     units), 4.7 (causal predicate col > row + (N_k - N_q)),
+ *     6.3 (block quantisation with per-tile descales), 6.4 (incoherent
+ *     processing with M = H D / sqrt(d)).
+ *   - "03 · FA3：Hopper 上的异步化与 overlap", section 4 (descales folded into
+ *     the softmax scale; Max_offset = 8 for FP8).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Layout   q, k, v, o are dense row-major [B, N, H, d] tensors (d fastest,
+ *            row stride H*d elements), the logical (batch, seqlen, head, dim)
+ *            order of the pages. lse is float32 [B, H, N]. N_q = N_k = N.
+ *   Pointers device pointers, 16-byte aligned; the caller allocates and owns
+ *            every buffer. o and lse must not overlap q, k or v.
+ *   Stream   every call is asynchronous on `stream` (a hipStream_t; NULL is
+ *            the default stream) and returns once its kernels are enqueued.
+ *   Errors   arguments are checked on the host before anything is launched;
+ *            a failing call returns a negative attn_status, launches nothing,
+ *            and leaves a message readable through attn_last_error().
+ *            N = 0 is a valid no-op. Nothing is printed, no exception
+ *            crosses the ABI.
+ *   State    the library keeps no state between calls except the
+ *            thread-local error message; it allocates no device memory.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad alpha */
+  ATTN_ERR_UNSUPPORTED = -2, /* valid request the library does not implement */
+  ATTN_ERR_HIP = -3          /* the HIP runtime reported an error */
+} attn_status;
+
+typedef enum {
+  ATTN_DTYPE_BF16 = 0, /* bfloat16 inputs and output */
+  ATTN_DTYPE_F16 = 1   /* IEEE binary16 inputs and output */
+} attn_dtype;
+
+/*
+ * attn_fwd -- exact attention forward, 16-bit inputs.
+ *
+ *   q, k, v  [B, N, H, d] in `dtype` (read only).
+ *   o        [B, N, H, d] in `dtype` (written): O = softmax(alpha q k^T) v,
+ *            each element rounded to nearest even from float32.
+ *   lse      [B, H, N] float32 (written): natural-log log-sum-exp of the
+ *            scaled, masked scores of each row; -inf for a row with no
+ *            visible key (whose O row is then 0).
+ *   B, H, N  >= 1 (N = 0 allowed: no-op).  B*N*H*d must fit in int64 and
+ *            B*H*N in int32 range.
+ *   d        64, 128 or 256 (other values: ATTN_ERR_UNSUPPORTED).
+ *   causal   0: every key visible; 1: key j is masked for query i when j > i.
+ *   alpha    softmax scale; finite and >= 0 (typically 1/sqrt(d)).
+ *   dtype    an attn_dtype.
+ *   stream   hipStream_t to launch on.
+ *
+ * Accumulation is float32; P is rounded to `dtype` before the P V product.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d, int causal, float alpha, int dtype,
+             void* stream);
+
+/*
+ * attn_fp8_prepare -- incoherent processing + block quantisation to e4m3.
+ *
+ *   x        [B, N, H, d] bfloat16 input (read only).
+ *   x8       [B, N, H, d] uint8 output: OCP e4m3 (e4m3fn) codes.
+ *   descale  float32 output: [B, H, ceil(N / block_rows)] when
+ *            block_rows = 128, or a single float when block_rows = 0
+ *            (one scale for the whole tensor).
+ *   block_rows  128 (per (b, h, 128-row block) scales) or 0 (per tensor).
+ *   hadamard 1: first replace each row x by x M with M = H D / sqrt(d)
+ *            (H the Sylvester-ordered +-1 Hadamard matrix, D the diagonal of
+ *            signs drawn from `hadamard_seed`), as for Q and K; 0: no
+ *            transform (always the case for V). d must be a power of two.
+ *   Scale rule: scale = amax / 448 over the block (1 if amax = 0);
+ *            code = round-to-nearest-even e4m3 of min(|y / scale|, 448) with
+ *            y's sign; descale = scale. All arithmetic is float32.
+ *   Signs:   sign[i] = -1 if bit 63 of splitmix64(hadamard_seed + i) is set,
+ *            else +1, where splitmix64(s) is the first output of a SplitMix64
+ *            generator with state s.
+ *
+ * The per-tensor case (block_rows = 0) reduces over the whole tensor in two
+ * kernels and needs no workspace: the second kernel recomputes the transform.
+ */
+int attn_fp8_prepare(const void* x, void* x8, float* descale,
+                     int B, int H, int N, int d, int block_rows,
+                     int hadamard, uint64_t hadamard_seed, void* stream);
+
+/*
+ * attn_fwd_fp8 -- exact attention forward on e4m3 inputs.
+ *
+ *   q8, k8, v8  [B, N, H, d] e4m3 codes from attn_fp8_prepare (q8 and k8
+ *            prepared with the same hadamard flag and seed; v8 without the
+ *            transform). Because (Q M)(K M)^T = Q K^T, the forward needs no
+ *            knowledge of M.
+ *   descale_q/k/v  float32 descales as written by attn_fp8_prepare with the
+ *            same block_rows.
+ *   o        [B, N, H, d] bfloat16 output; lse [B, H, N] float32.
+ *   block_rows  128 or 0, matching the descales.
+ *   Other arguments as attn_fwd (d = 64, 128 or 256).
+ *
+ * Scores are accumulated in float32 and multiplied by alpha * dq * dk per
+ * tile; P is formed as exp2 of the shifted score plus Max_offset = 8 and
+ * rounded to e4m3 for the P V product, whose result is multiplied by dv.
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float alpha,
+                 const float* descale_q, const float* descale_k, const float* descale_v,
+                 int block_rows, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next call on the same thread. */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

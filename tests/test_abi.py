@@ -1,0 +1,132 @@
+"""C ABI contract (runs without a GPU).
+
+The library must load, export every function include/attn.h declares, and
+reject bad arguments with the documented status before launching anything.
+Only argument combinations that fail validation are passed here, so no
+kernel is ever launched on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_forward_attn_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ea.lib_path), reason="libattn.so not built")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert header_functions() == sorted(ea.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ea.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.attn_version().decode().startswith("attn-gfx950")
+
+
+def _fwd(**kw):
+    lib = ea.load()
+    a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000,
+             lse=FAKE + 0x40000000, B=1, H=2, N=256, d=64, causal=0, alpha=0.125, dtype=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                        a["alpha"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(d=32), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(dtype=2), ea.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(q=None), ea.ATTN_ERR_INVALID_ARG, "q is null"),
+    (dict(lse=None), ea.ATTN_ERR_INVALID_ARG, "lse is null"),
+    (dict(v=FAKE + 8), ea.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(B=-1), ea.ATTN_ERR_INVALID_ARG, ">= 0"),
+    (dict(N=-5), ea.ATTN_ERR_INVALID_ARG, ">= 0"),
+    (dict(causal=2), ea.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(alpha=float("nan")), ea.ATTN_ERR_INVALID_ARG, "alpha"),
+    (dict(alpha=float("inf")), ea.ATTN_ERR_INVALID_ARG, "alpha"),
+    (dict(alpha=-0.5), ea.ATTN_ERR_INVALID_ARG, "alpha"),
+    (dict(o=FAKE + 0x100), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
+    (dict(lse=FAKE + 0x20000000 + 64), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
+    (dict(N=1 << 20, H=64, d=256), ea.ATTN_ERR_UNSUPPORTED, "too large"),
+])
+def test_fwd_rejects_bad_arguments_before_launch(kw, status, msg):
+    assert _fwd(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def test_empty_problems_are_valid_no_ops():
+    for kw in (dict(N=0), dict(B=0), dict(H=0)):
+        assert _fwd(**kw) == ea.ATTN_OK
+        assert ea.attn_last_error() == ""
+
+
+def test_error_message_is_cleared_by_next_success():
+    assert _fwd(d=96) == ea.ATTN_ERR_UNSUPPORTED
+    assert _fwd(N=0) == ea.ATTN_OK
+    assert ea.attn_last_error() == ""
+
+
+def _prep(**kw):
+    lib = ea.load()
+    a = dict(x=FAKE, x8=FAKE + 0x10000000, descale=FAKE + 0x20000000, B=1, H=2, N=256, d=128, block_rows=128,
+             hadamard=1, seed=0, stream=None)
+    a.update(kw)
+    return lib.attn_fp8_prepare(a["x"], a["x8"], a["descale"], a["B"], a["H"], a["N"], a["d"], a["block_rows"],
+                                a["hadamard"], ctypes.c_uint64(a["seed"]), a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(block_rows=64), ea.ATTN_ERR_INVALID_ARG, "block_rows"),
+    (dict(hadamard=3), ea.ATTN_ERR_INVALID_ARG, "hadamard"),
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(x8=None), ea.ATTN_ERR_INVALID_ARG, "x8 is null"),
+    (dict(descale=FAKE + 4), ea.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(x8=FAKE + 64), ea.ATTN_ERR_INVALID_ARG, "overlaps"),
+])
+def test_prepare_rejects_bad_arguments(kw, status, msg):
+    assert _prep(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def _fwd8(**kw):
+    lib = ea.load()
+    a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000, lse=FAKE + 0x40000000,
+             B=1, H=2, N=256, d=128, causal=0, alpha=0.1, dq=FAKE + 0x50000000, dk=FAKE + 0x50001000,
+             dv=FAKE + 0x50002000, block_rows=128, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                            a["causal"], a["alpha"], a["dq"], a["dk"], a["dv"], a["block_rows"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(block_rows=32), ea.ATTN_ERR_INVALID_ARG, "block_rows"),
+    (dict(dk=None), ea.ATTN_ERR_INVALID_ARG, "descale_k is null"),
+    (dict(d=80), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(alpha=float("-inf")), ea.ATTN_ERR_INVALID_ARG, "alpha"),
+])
+def test_fp8_forward_rejects_bad_arguments(kw, status, msg):
+    assert _fwd8(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def test_binding_has_no_cpu_fallback(monkeypatch):
+    # with the library path pointing nowhere the binding must raise, not compute
+    monkeypatch.setattr(ea, "lib_path", "/nonexistent/libattn.so")
+    monkeypatch.setattr(ea, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        ea.load()

@@ -1,0 +1,133 @@
+"""GPU parity of the 16-bit forward against the float64 oracle.
+
+Small shapes (several tiles plus ragged tails) are compared element by
+element over the whole output; the full benchmark shapes are compared on
+sampled query rows that the oracle computes one by one, plus properties that
+hold at any size. Tolerances: max |O - O_ref| <= 1e-2, RMSE(O) <= 3e-3,
+max |LSE - LSE_ref| <= 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_bf16_tolerances, device_qkv, errors, to_f64
+from oracle.attention import attention, attention_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def run(ea, q, k, v, causal, alpha=None):
+    import torch
+    o, lse = ea.attention(q, k, v, causal=causal, alpha=alpha)
+    torch.cuda.synchronize()
+    return to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def test_tiny_config_matches_oracle(gpu):
+    # B=1, H=2, N=256, d=64, non-causal, alpha = 1/sqrt(d), seed 0
+    (q, k, v), (qf, kf, vf) = device_qkv(1, 256, 2, 64, seed=0)
+    o, lse = run(gpu, q, k, v, False)
+    o_ref, l_ref = attention(qf, kf, vf, 1 / 8, False)
+    err = errors(o, o_ref, lse, l_ref)
+    print("tiny", err)
+    assert_bf16_tolerances(err, "tiny")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 129, 300, 777])
+def test_small_shapes_full_output(gpu, d, causal, N):
+    B, H = 2, 3
+    (q, k, v), (qf, kf, vf) = device_qkv(B, N, H, d, seed=N + d)
+    o, lse = run(gpu, q, k, v, causal)
+    o_ref, l_ref = attention(qf, kf, vf, 1 / math.sqrt(d), causal)
+    err = errors(o, o_ref, lse, l_ref)
+    assert_bf16_tolerances(err, (d, causal, N))
+
+
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False), (256, True)])
+def test_float16_inputs(gpu, d, causal):
+    (q, k, v), (qf, kf, vf) = device_qkv(1, 200, 2, d, seed=3, dtype="f16")
+    o, lse = run(gpu, q, k, v, causal)
+    o_ref, l_ref = attention(qf, kf, vf, 1 / math.sqrt(d), causal)
+    assert_bf16_tolerances(errors(o, o_ref, lse, l_ref), "f16")
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.05, 0.3])
+def test_other_softmax_scales(gpu, alpha):
+    (q, k, v), (qf, kf, vf) = device_qkv(1, 300, 2, 128, seed=4)
+    for causal in (False, True):
+        o, lse = run(gpu, q, k, v, causal, alpha=alpha)
+        o_ref, l_ref = attention(qf, kf, vf, alpha, causal)
+        assert_bf16_tolerances(errors(o, o_ref, lse, l_ref), (alpha, causal))
+
+
+def test_large_scores_stay_finite(gpu):
+    # scores up to ~1e3 exercise the running-max rescale
+    import torch
+    (q, k, v), (qf, kf, vf) = device_qkv(1, 500, 2, 128, seed=6)
+    q = (q.float() * 30).to(torch.bfloat16)
+    qf = to_f64(q)
+    o, lse = run(gpu, q, k, v, True)
+    o_ref, l_ref = attention(qf, kf, vf, 1 / math.sqrt(128), True)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    err = errors(o, o_ref, lse, l_ref)
+    assert err["max_abs"] <= 2e-2 and err["rmse"] <= 3e-3, err
+    assert err["lse_abs"] <= 2e-3 * max(1.0, np.abs(l_ref).max() / 100), err
+
+
+def test_repeated_launches_are_bitwise_identical(gpu):
+    import torch
+    (q, k, v), _ = device_qkv(2, 1000, 4, 128, seed=7)
+    ref = gpu.attention(q, k, v, causal=True)
+    for _ in range(10):
+        o, lse = gpu.attention(q, k, v, causal=True)
+        assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+
+
+def test_empty_sequence_is_a_no_op(gpu):
+    import torch
+    q = torch.zeros((2, 0, 3, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = gpu.attention(q, q, q)
+    assert o.shape == (2, 0, 3, 64) and lse.shape == (2, 3, 0)
+
+
+def sample_rows(N, rng, extra=24):
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, N // 2, N - 129, N - 65, N - 2, N - 1]
+    rows = set(r for r in fixed if 0 <= r < N)
+    rows.update(rng.integers(0, N, size=extra).tolist())
+    return np.array(sorted(rows))
+
+
+def check_sampled(ea, B, N, H, d, causals, seed=0, heads=3):
+    (q, k, v), (qf, kf, vf) = device_qkv(B, N, H, d, seed=seed)
+    vmax = np.abs(vf).max()
+    rng = np.random.default_rng(seed + N)
+    pairs = {(0, 0), (B - 1, H - 1)}
+    while len(pairs) < min(heads, B * H):
+        pairs.add((int(rng.integers(B)), int(rng.integers(H))))
+    for causal in causals:
+        o, lse = run(ea, q, k, v, causal)
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        assert np.abs(o).max() <= vmax * 1.01
+        samples = [(b, h, sample_rows(N, rng)) for b, h in sorted(pairs)]
+        refs = attention_rows(qf, kf, vf, 1 / math.sqrt(d), causal, samples)
+        og = np.concatenate([o[b, rows, h] for b, h, rows in samples])
+        lg = np.concatenate([lse[b, h, rows] for b, h, rows in samples])
+        orf = np.concatenate([r[0] for r in refs])
+        lrf = np.concatenate([r[1] for r in refs])
+        err = errors(og, orf, lg, lrf)
+        print((B, N, H, d, causal), err, flush=True)
+        assert_bf16_tolerances(err, (B, N, H, d, causal))
+
+
+# hidden 2048, 16k tokens: d=64 with H=32 and d=128 with H=16
+@pytest.mark.parametrize("d,H", [(64, 32), (128, 16), (256, 8)])
+@pytest.mark.parametrize("N", [512, 1024, 2048, 4096, 8192, 16384])
+def test_sweep_configs_sampled(gpu, d, H, N):
+    check_sampled(gpu, 16384 // N, N, H, d, (False, True))
+
+
+def test_long_causal_sampled(gpu):
+    check_sampled(gpu, 1, 32768, 16, 128, (True,), heads=2)
