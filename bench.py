@@ -1,0 +1,261 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+A step is one attention forward over one batch of synthetic inputs already
+resident in HBM, at the headline configuration: bf16, d=128, N=8192, B=2,
+H=16 (16k tokens, hidden 2048), non-causal. Throughput is reported in
+TFLOP/s with the pages' FLOP convention, 4*B*H*N^2*d (halved for causal).
+
+Prints ONE JSON line (metric, value, roofline, cpu_baseline, ...). Extra
+measurements (the sequence-length sweep, FP8) go to stderr, and to a JSON
+file when --out is given.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8]
+       python bench.py --copy-calibration   (plain copy kernel for PMC scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOPS + % of MFMA peak, bf16 d=128 N=8k (and fp8)"
+HEADLINE = dict(B=2, N=8192, H=16, d=128, causal=False)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_d128_n8192.json")
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_forward_attn_amd", "csrc", "attn_fwd.hip")
+
+
+def flops(B, N, H, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def device_inputs(B, N, H, d, seed=0, outliers=None):
+    import numpy as np
+    import torch
+    from synth_inputs import make_qkv_f32
+    # Draws in float32 then rounds on the device (same RNE rounding as the
+    # synth_inputs bf16 cast; timing only needs realistic N(0,1) values).
+    q, k, v = make_qkv_f32(B, N, H, d, seed=seed, outliers=outliers)
+    return [torch.from_numpy(t).cuda().to(torch.bfloat16) for t in (q, k, v)]
+
+
+def time_launches(fn, steps, warmup):
+    """Runs fn warmup + steps times; returns (total_ms, per-launch ms list)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+
+
+def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
+    import torch
+    q, k, v = device_inputs(B, N, H, d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = lambda: ea.attn_fwd(q, k, v, o, lse, causal=causal)
+    total, per = time_launches(fn, steps, warmup)
+    per_ms = sum(per) / len(per)
+    tf = flops(B, N, H, d, causal) / (per_ms * 1e-3) / 1e12
+    return {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "ms_total": total,
+            "TFLOPS": tf, "frac_peak": tf / PEAK_TFLOPS["bf16"],
+            "hbm_GBs": 8.0 * B * N * H * d / (per_ms * 1e-3) / 1e9}
+
+
+def bench_fp8(ea, B, N, H, d, causal, steps, warmup):
+    import torch
+    q, k, v = device_inputs(B, N, H, d, outliers={"rate": 1e-3, "factor": 10.0, "kind": "scale"})
+    q8, sq = ea.fp8_prepare(q, 128, True, 0)
+    k8, sk = ea.fp8_prepare(k, 128, True, 0)
+    v8, sv = ea.fp8_prepare(v, 128, False, 0)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = lambda: ea.attn_fwd_fp8(q8, k8, v8, o, lse, sq, sk, sv, causal=causal)
+    total, per = time_launches(fn, steps, warmup)
+    per_ms = sum(per) / len(per)
+    tf = flops(B, N, H, d, causal) / (per_ms * 1e-3) / 1e12
+    prep = lambda: ea.attn_fp8_prepare(q, q8, sq, 128, True, 0)
+    _, pper = time_launches(prep, max(3, steps // 2), 2)
+    return {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "TFLOPS": tf,
+            "frac_peak": tf / PEAK_TFLOPS["fp8"], "prepare_ms_per_tensor": sum(pper) / len(pper)}
+
+
+def cpu_baseline(target_s=15.0):
+    """Times the float64 oracle on the host on a bounded sample of the
+    headline workload: whole (b, h) heads (all N query rows, all keys) until
+    ~target_s seconds are spent; reports TFLOP/s with the same FLOP count."""
+    import numpy as np
+    from oracle.attention import attention_head
+    from synth_inputs import make_qkv
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cfg = HEADLINE
+    B, N, H, d = cfg["B"], cfg["N"], cfg["H"], cfg["d"]
+    # inputs of the first head only: the other heads are identical in cost
+    _, (q, k, v) = make_qkv(1, N, 1, d, seed=0)
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        attention_head(q[0, :, 0], k[0, :, 0], v[0, :, 0], 1 / math.sqrt(d), cfg["causal"])
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or heads >= B * H:
+            break
+    per_head_flops = flops(1, N, 1, d, cfg["causal"])
+    tf = heads * per_head_flops / el / 1e12
+    return {"value": tf, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {B * H} (b,h) heads at N={N}, d={d}, full rows, numpy float64 "
+                      f"({el:.1f} s); rate extrapolates linearly over heads"}
+
+
+def traffic_entry():
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except Exception:
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true", help="also time the 16k-token sweep (stderr)")
+    ap.add_argument("--fp8", action="store_true", help="also time the FP8 forward (stderr)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this attention forward build has no multi-GPU path "
+              "(heads and batch shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    import exact_attention_forward_attn_amd as ea
+    ea.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    h = HEADLINE
+    head = bench_bf16(ea, h["B"], h["N"], h["H"], h["d"], h["causal"], args.steps, args.warmup)
+    log("headline", json.dumps(head))
+    extra = {"headline": head}
+
+    if args.sweep:
+        rows = []
+        for d, H in ((64, 32), (128, 16), (256, 8)):
+            for N in (512, 1024, 2048, 4096, 8192, 16384):
+                for causal in (False, True):
+                    r = bench_bf16(ea, 16384 // N, N, H, d, causal, max(5, args.steps // 2), 2)
+                    log("sweep", json.dumps(r))
+                    rows.append(r)
+        r = bench_bf16(ea, 1, 32768, 16, 128, True, 5, 2)
+        log("long", json.dumps(r))
+        rows.append(r)
+        extra["sweep"] = rows
+    fp8_res = None
+    if args.fp8:
+        try:
+            fp8_res = []
+            for N in (1024, 2048, 4096, 8192, 16384):
+                r = bench_fp8(ea, 16384 // N, N, 16, 128, False, max(5, args.steps // 2), 2)
+                log("fp8", json.dumps(r))
+                fp8_res.append(r)
+            extra["fp8"] = fp8_res
+        except ea.AttnError as e:
+            log("fp8 unavailable:", e)
+            fp8_res = None
+
+    cpu = None if args.no_cpu else cpu_baseline()
+    if cpu:
+        log("cpu_baseline", json.dumps(cpu))
+
+    fl = flops(h["B"], h["N"], h["H"], h["d"], h["causal"])
+    achieved = fl / (head["ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(head["TFLOPS"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_total"] / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: Q, K, V i.i.d. N(0,1) rounded to bf16, seed 0",
+        "config": {"workload": "exact attention forward, bf16, d=128, N=8192, B=2, H=16 "
+                               "(16k tokens, hidden 2048), non-causal",
+                   "global_batch": h["B"], "seq_len": h["N"], "heads": h["H"], "head_dim": h["d"],
+                   "causal": h["causal"], "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": traffic_entry()},
+        "cpu_baseline": cpu,
+    }
+    if fp8_res:
+        best = [r for r in fp8_res if r["N"] == 8192]
+        line["fp8"] = {"TFLOPS": round(best[0]["TFLOPS"], 2), "frac_peak": round(best[0]["frac_peak"], 4),
+                       "config": "e4m3, block 128 + Hadamard, d=128, N=8192, B=2, H=16, non-causal"} if best else None
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump({"line": line, **extra}, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
