@@ -43,22 +43,12 @@
 #include <stdint.h>
 
 #include "attn_internal.h"
+#include "kernel_common.h"
 
 namespace attn {
 namespace fwd16 {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-#define LDS_AS __attribute__((address_space(3)))
-
-constexpr float kLn2 = 0.693147180559945309f;
+using namespace attn::dev;
 
 template <typename T>
 struct Elt;
@@ -107,39 +97,11 @@ struct Geo {
 // transposing load, 4 rows x 4 chunks per 16 lanes.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
-  return D == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : (r & 15);
+  return swz_rows<2 * D>(r);
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
-}
-
-// Combine x across lanes l and l+32. v_permlane32_swap with both operands
-// equal to x returns, per lane, the pair {x of lanes 0-31, x of lanes 32-63}
-// of its column, i.e. {x[l], x[l+32]} for l < 32 and {x[l-32], x[l]} above;
-// a symmetric op over the pair is the cross-half reduction.
-__device__ __forceinline__ float halves_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 #ifndef ATTN_SB_K
@@ -148,13 +110,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 #ifndef ATTN_SB_V
 #define ATTN_SB_V 2
 #endif
-
-struct TrueT {
-  static constexpr bool value = true;
-};
-struct FalseT {
-  static constexpr bool value = false;
-};
 
 struct KernelArgs {
   const void* q;
@@ -193,23 +148,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
 
   // ---- work decomposition -------------------------------------------------
   const int BH = a.B * a.H;
-  const int nblk = a.n_mblk * BH;
   int mblk, bh;
-  if (CAUSAL) {
-    // longest-processing-time first: the last query blocks see the most keys
-    const int L = blockIdx.x;
-    mblk = a.n_mblk - 1 - L / BH;
-    bh = L % BH;
-  } else {
-    // consecutive workgroup ids go round-robin over the 8 XCDs; renumber so
-    // each XCD receives a contiguous range of (head, query-block) work
-    const int w = blockIdx.x;
-    const int per = nblk / 8, rem = nblk % 8;
-    const int x = w % 8, kk = w / 8;
-    const int L = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + kk;
-    mblk = L % a.n_mblk;
-    bh = L / a.n_mblk;
-  }
+  decode_block(blockIdx.x, a.n_mblk, BH, CAUSAL, mblk, bh);
   const int b = bh / a.H;
   const int hh = bh % a.H;
   const int N = a.N;

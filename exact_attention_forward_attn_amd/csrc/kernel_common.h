@@ -1,0 +1,93 @@
+// Device helpers shared by the attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+namespace dev {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLn2 = 0.693147180559945309f;
+
+struct TrueT {
+  static constexpr bool value = true;
+};
+struct FalseT {
+  static constexpr bool value = false;
+};
+
+// s_waitcnt with only the vector-memory counter constrained (<= N in flight).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Combine x across lanes l and l+32. v_permlane32_swap with both operands
+// equal to x returns, per lane, the pair {x of lanes 0-31, x of lanes 32-63}
+// of its column, i.e. {x[l], x[l+32]} for l < 32 and {x[l-32], x[l]} above;
+// a symmetric op over the pair is the cross-half reduction.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// v_exp_f32 (2^x) without range reduction; outputs below 2^-126 flush to 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Workgroup id -> (query block, batch*head). Causal grids go longest first
+// (the last query blocks see the most keys); non-causal grids are renumbered
+// so that each of the 8 XCDs (which receive workgroup ids round-robin) gets
+// a contiguous range, keeping one head's query blocks on one L2.
+__device__ __forceinline__ void decode_block(int w, int n_mblk, int BH, bool causal, int& mblk, int& bh) {
+  if (causal) {
+    mblk = n_mblk - 1 - w / BH;
+    bh = w % BH;
+  } else {
+    const int nblk = n_mblk * BH;
+    const int per = nblk / 8, rem = nblk % 8;
+    const int x = w % 8, kk = w / 8;
+    const int L = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + kk;
+    mblk = L % n_mblk;
+    bh = L / n_mblk;
+  }
+}
+
+// XOR swizzle of the 16-byte chunk index of LDS row r, for rows of ROWB bytes
+// that are read 32 rows x one chunk per instruction: 16 consecutive rows land
+// on 16 different bank groups.
+template <int ROWB>
+__device__ __forceinline__ int swz_rows(int r) {
+  static_assert(ROWB == 64 || ROWB == 128 || ROWB >= 256, "row size");
+  return ROWB >= 256 ? (r & 15) : ROWB == 128 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
+}
+
+}  // namespace dev
+}  // namespace attn
