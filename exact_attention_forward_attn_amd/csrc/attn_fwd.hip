@@ -63,6 +63,16 @@ struct Elt<__bf16> {
   static __device__ __forceinline__ v4 tr_read(const LDS_AS char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4*)p);
   }
+  // acc + sum of the eight 16-bit values (v_dot2 against (1, 1), fp32 sum)
+  static __device__ __forceinline__ float sum8(v8 x, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    struct P4 { b2 p[4]; };
+    const P4 pr = __builtin_bit_cast(P4, x);
+    const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(pr.p[i], one, acc, false);
+    return acc;
+  }
 };
 
 template <>
@@ -75,6 +85,15 @@ struct Elt<_Float16> {
   typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
   static __device__ __forceinline__ v4 tr_read(const LDS_AS char* p) {
     return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS raw4*)p));
+  }
+  static __device__ __forceinline__ float sum8(v8 x, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    struct P4 { h2 p[4]; };
+    const P4 pr = __builtin_bit_cast(P4, x);
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(pr.p[i], one, acc, false);
+    return acc;
   }
 };
 
@@ -104,6 +123,11 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
 }
 
+#ifndef ATTN_LAZY_RESCALE
+#define ATTN_LAZY_RESCALE 1
+#endif
+// rescale threshold of the lazy path, in base-2 exponent units
+constexpr float kTau = 8.0f;
 #ifndef ATTN_SB_K
 #define ATTN_SB_K 4
 #endif
@@ -122,8 +146,8 @@ struct KernelArgs {
   float c;        // alpha * log2(e)
 };
 
-template <int D, int QB, int KB, bool CAUSAL, typename T>
-__global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
+template <int D, int QB, int KB, bool CAUSAL, bool PP, typename T>
+__global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   // The body is device code only; the host pass just needs the launch stub
   // (instantiating the body there makes clang drop the stub silently).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -133,18 +157,29 @@ __global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
   typedef Geo<D, KB> G;
   constexpr int BN = G::BN;
   constexpr int WQ = 32 * QB;         // query rows per wave
-  constexpr int BM = 4 * WQ;          // query rows per workgroup
+  constexpr int WAVES = PP ? 8 : 4;   // ping-pong: two groups of four waves
+  constexpr int BM = WAVES * WQ;      // query rows per workgroup
   constexpr int KC = D / 16;          // k-steps of the QK^T product
   constexpr int KCL = KC < 8 ? KC : 8;
   constexpr int DB = D / 32;          // 32-dim blocks of O
   constexpr int DBL = DB < 4 ? DB : 4;
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+  // Two K slots and two V slots, each its own object: slot choice is a
+  // compile-time parity below, so the compiler can see that a copy into one
+  // slot never aliases reads of another and need not serialise them.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[G::TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h32 = lane >> 5;   // which half of the wave
   const int l32 = lane & 31;
+  // Group 0 (waves 0-3) issues every K/V copy; with ping-pong, group 1
+  // (waves 4-7) runs one phase behind it.
+  const int grp = PP ? (wave >> 2) : 0;
+  const int lw = wave & 3;     // wave index within its group (copy segments)
 
   // ---- work decomposition -------------------------------------------------
   const int BH = a.B * a.H;
@@ -176,15 +211,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
   }
 
   // ---- per-lane LDS offsets -------------------------------------------------
-  // global -> LDS copy: segment seg, lane i covers row seg*RPS + i/CPR, chunk i%CPR
-  uint32_t kg[G::SEG_PER_WAVE], vg[G::SEG_PER_WAVE];
+  // global -> LDS copy: segment seg = lw + 4t, lane i covers row seg*RPS + i/CPR,
+  // chunk i%CPR. The swizzles depend on the row modulo 16 (K) or 4 (V); a step
+  // of t moves the row by 4*RPS, which keeps both except for K rows of 512
+  // bytes (RPS = 2), where the parity of t matters. So one per-lane base
+  // (two for that K case) plus a uniform per-segment stride covers all t.
+  constexpr int KGP = (G::RPS * 4) % 16 == 0 ? 1 : 2;
+  uint32_t kg[KGP], vg0;
 #pragma unroll
-  for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
-    const int seg = wave + 4 * t;
-    const int r = seg * G::RPS + lane / G::CPR;
+  for (int t = 0; t < KGP; ++t) {
+    const int r = (lw + 4 * t) * G::RPS + lane / G::CPR;
     const int pc = lane % G::CPR;
-    kg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_k<D>(r)) << 4);
-    vg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_v<D>(r)) << 4);
+    kg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * 4 * G::RPS * RS;
+  }
+  {
+    const int r = lw * G::RPS + lane / G::CPR;
+    const int pc = lane % G::CPR;
+    vg0 = (uint32_t)r * RS + (uint32_t)((pc ^ swz_v<D>(r)) << 4);
   }
   // K operand reads: row kb*32 + l32, logical chunk 2kc + h32
   int kofs[KCL];
@@ -204,11 +247,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
 
   // ---- online softmax state -------------------------------------------------
   f32x16 oacc[QB][DB];
-  float m_run[QB], l_run[QB];
+  // m_run: running max (the exponent reference); l_run: sum of the rounded P
+  // that entered P V (normalises O); l_lse: float32 sum of P (gives LSE)
+  float m_run[QB], l_run[QB], l_lse[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -__builtin_inff();
     l_run[qb] = 0.f;
+    l_lse[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
   }
@@ -216,52 +262,131 @@ __global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;
+  // Processing order i = 0 .. nt-1 visits KV tile j = nt-1-i (descending).
+  // The tiles this wave must mask (tail past N, keys right of its diagonal)
+  // form a prefix of that order: tile j is masked iff j >= jm.
+  int jm = N >= BN ? (N - BN) / BN + 1 : 0;
+  if (CAUSAL) {
+    const int x = qw - BN + 1;
+    jm = min(jm, x >= 0 ? x / BN + 1 : 0);
+  }
+  const int n_masked = max(0, nt - jm);
 
-  auto issue_tile = [&](int kv0, int st) {
-    const uint32_t base = (uint32_t)kv0 * RS;
+  // LDS: two K slots then two V slots. K runs one tile ahead of V: while
+  // tile i's V and tile i+1's K are read, tile i+1's V and tile i+2's K load.
+  auto kslot = [&](auto par) -> char* { return decltype(par)::value ? kbuf1 : kbuf0; };
+  auto vslot = [&](auto par) -> char* { return decltype(par)::value ? vbuf1 : vbuf0; };
+  // Copy tile i (in processing order) of K or V into dst. The row offset of
+  // segment t is the per-lane base plus a uniform stride; the base goes
+  // through an empty asm so the compiler cannot hoist one VGPR per
+  // (slot, segment) out of the loop.
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) {
+    const uint32_t base = (uint32_t)((nt - 1 - i) * BN) * RS;
+    uint32_t g0 = is_k ? kg[0] : vg0;
+    uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
+    asm volatile("" : "+v"(g0), "+v"(g1));
 #pragma unroll
     for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
-      const int seg = wave + 4 * t;
-      char* kdst = smem + st * G::STAGE + seg * 1024;
-      char* vdst = smem + st * G::STAGE + G::TILE + seg * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)kdst, 16, base + kg[t], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)vdst, 16, base + vg[t], 0, 0, 0);
+      const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * 4 * G::RPS * RS);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (lw + 4 * t) * 1024), 16, voff, 0, 0, 0);
     }
   };
+  // Workgroup barrier at a phase boundary. Every LDS read of this wave has
+  // landed first (the compiler may otherwise sink the barrier above a pending
+  // ds_read), and no work crosses it in either direction.
+  auto barrier = [&]() {
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Start of a tile's MFMA phase: the copies group 0 issued two phases ago
+  // have landed (its own wait, then the barrier publishes them).
+  auto sync_tile = [&]() {
+    if (grp == 0) wait_vmcnt<0>();
+    barrier();
+  };
+  auto phase_barrier = [&]() {
+    if (PP) barrier();
+  };
 
-  // One KV tile: S^T, (mask), online softmax, O^T += V^T P^T.
-  auto process = [&](const char* kt, const LDS_AS char* vt, int kv0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 s[KB][QB];
+  f32x16 s[KB][QB];
+  v8 pk[KB][QB][2];
+
+  // S^T = K Q^T for one tile (QK only: the prologue)
+  auto qk = [&](const char* kt) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if (kc % ATTN_SB_K == 0) __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < KC * KB; ++t) {
+      const int kc = t / KB, kb = t % KB;
+      const v8 ka = *(const v8*)(kt + kb * 32 * G::ROWB + (kc / 8) * 256 + kofs[kc % 8]);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma(ka, qreg[qb][kc], s[kb][qb]);
+    }
+  };
+
+  // The MFMA phase of one iteration: O^T += V^T P^T for the current tile,
+  // interleaved with S^T = K Q^T for the next one (the pages' intra-warpgroup
+  // overlap: GEMM1 of tile i and GEMM0 of tile i+1 are independent).
+  auto mfma_phase = [&](const LDS_AS char* vt, const char* kt, auto do_qk_tag) {
+    constexpr bool DO_QK = decltype(do_qk_tag)::value;
+    // O^T += V^T P^T first (P dies), then S^T = K Q^T (S is born): the two
+    // never need registers at the same time
+    constexpr int STEPS = DB * KB * 2;  // == KC * KB
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      if (t % ATTN_SB_V == 0) __builtin_amdgcn_sched_barrier(0);
+      const int db = t / (2 * KB), kb = (t / 2) % KB, ks = t % 2;
+      const LDS_AS char* pv = vt + (kb * 32 + 16 * ks) * G::ROWB + (db / 4) * 256 + vofs[db % 4];
+      const v4 lo = E::tr_read(pv);
+      const v4 hi = E::tr_read(pv + 8 * G::ROWB);
+      const v8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(va, pk[kb][qb][ks], oacc[qb][db]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (DO_QK) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KC * KB; ++t) {
+        if (t % ATTN_SB_K == 0) __builtin_amdgcn_sched_barrier(0);
+        const int kc = t / KB, kb = t % KB;
         const v8 ka = *(const v8*)(kt + kb * 32 * G::ROWB + (kc / 8) * 256 + kofs[kc % 8]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma(ka, qreg[qb][kc], s[kb][qb]);
       }
     }
-    if (MASKED) {
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Online softmax of the scores in s (tile starting at key kv0): running
+  // max, P = 2^(s c - m c) packed to 16 bits in pk, l, and the O rescale.
+  // Scores of keys past N or right of the diagonal become -inf (only the
+  // tiles of the masked prefix call this).
+  auto apply_mask = [&](int kv0) {
+    // key offset within the tile = 4*h32 + o with o a compile-time constant,
+    // so compare o against per-lane thresholds (no per-element index vectors)
+    const int tn = N - kv0 - 4 * h32;  // o >= tn: key at or past N
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw + qb * 32 + l32;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int tc = qw + qb * 32 + l32 - kv0 - 4 * h32;  // o > tc: key right of the diagonal
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            const bool bad = key >= N || (CAUSAL && key > qi);
-            if (bad) s[kb][qb][r] = -__builtin_inff();
-          }
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
+          if (o >= tn || (CAUSAL && o > tc)) s[kb][qb][r] = -__builtin_inff();
+        }
     }
-    typename E::v8 pk[KB][QB][2];
+  };
+
+  auto softmax = [&]() {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = s[0][qb][0];
@@ -270,91 +395,117 @@ __global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][qb][r]);
       mx = halves_max(mx);
+#if ATTN_LAZY_RESCALE
+      // Conditional rescale ("FlashAttention v1-v4", FA4 section): m_run is
+      // the reference the exponents are taken against. It only moves when
+      // some row's maximum exceeds it by more than kTau base-2 units, so
+      // p <= 2^kTau, and O~ and l are rescaled only then. O = O~/l and
+      // LSE = m c + log2 l are unchanged in exact arithmetic.
+      const float mref = m_run[qb];
+      if (__builtin_amdgcn_ballot_w64((mx - mref) * c > kTau) != 0) {
+        const float m_new = __builtin_fmaxf(mref, mx);
+        const float rho = (m_new == -__builtin_inff()) ? 1.f : exp2_fast((mref - m_new) * c);
+        m_run[qb] = m_new;
+        l_run[qb] *= rho;
+        l_lse[qb] *= rho;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[qb][db] *= rho;
+      }
+      const float ms = (m_run[qb] == -__builtin_inff()) ? 0.f : m_run[qb] * c;
+#else
       const float m_new = __builtin_fmaxf(m_run[qb], mx);
       const float ms = (m_new == -__builtin_inff()) ? 0.f : m_new * c;
       const float rho = exp2_fast(m_run[qb] * c - ms);
       m_run[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(__builtin_fmaf(s[kb][qb][r], c, -ms));
-          s[kb][qb][r] = p;
-          rs += p;
-        }
-      l_run[qb] = l_run[qb] * rho + rs;
-      // the rescale is skipped when no row of the wave changed its maximum
-      if (__builtin_amdgcn_ballot_w64(rho != 1.0f) != 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[qb][db] *= rho;
-      }
+      l_run[qb] *= rho;
+      l_lse[qb] *= rho;
+#endif
+      // P = 2^(s c - m c), rounded to 16 bits in place: these registers are
+      // the B operand of the next P V product. l sums the rounded values, so
+      // O~/l is an exact convex combination of the weights the product used.
+      float rs = 0.f, rs32 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           f32x8 f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = s[kb][qb][8 * ks + e];
-          pk[kb][qb][ks] = __builtin_convertvector(f, typename E::v8);
+          for (int e = 0; e < 8; ++e) {
+            f[e] = exp2_fast(__builtin_fmaf(s[kb][qb][8 * ks + e], c, -ms));
+            rs32 += f[e];
+          }
+          pk[kb][qb][ks] = __builtin_convertvector(f, v8);
+          rs = E::sum8(pk[kb][qb][ks], rs);
         }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      l_run[qb] += rs;
+      l_lse[qb] += rs32;
+#if !ATTN_LAZY_RESCALE
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      if (db % ATTN_SB_V == 0) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const LDS_AS char* pv = vt + (kb * 32 + 16 * ks) * G::ROWB + (db / 4) * 256 + vofs[db % 4];
-          const v4 lo = E::tr_read(pv);
-          const v4 hi = E::tr_read(pv + 8 * G::ROWB);
-          const v8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(va, pk[kb][qb][ks], oacc[qb][db]);
-        }
+      for (int db = 0; db < DB; ++db) oacc[qb][db] *= rho;
+#endif
     }
   };
 
-  if (nt > 0) issue_tile((nt - 1) * BN, 0);
-  for (int it = 0; it < nt; ++it) {
-    const int j = nt - 1 - it;
-    const int kv0 = j * BN;
-    const int st = it & 1;
-    if (it + 1 < nt) {
-      issue_tile(kv0 - BN, st ^ 1);
-      wait_vmcnt<2 * G::SEG_PER_WAVE>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    const bool skip = (CAUSAL && kv0 > qw + WQ - 1) || qw >= N;
-    if (!skip) {
-      const char* kt = smem + st * G::STAGE;
-      const LDS_AS char* vt = (const LDS_AS char*)(smem + st * G::STAGE + G::TILE);
-      const bool masked = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > qw);
-      if (masked)
-        process(kt, vt, kv0, TrueT{});
-      else
-        process(kt, vt, kv0, FalseT{});
-    }
-    // every LDS read of this stage must have landed before any wave refills it
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
+  // Ping-pong: group 1 takes one extra barrier first so its phases trail
+  // group 0's by one; group 0 takes one extra at the end to match the count.
+  if (PP && grp == 1) barrier();
+
+  // prologue: K and V of tile 0, K of tile 1; S and P of tile 0
+  if (grp == 0) {
+    issue(rk, true, kslot(FalseT{}), 0);
+    issue(rv, false, vslot(FalseT{}), 0);
+    if (nt > 1) issue(rk, true, kslot(TrueT{}), 1);
   }
+  sync_tile();
+  qk(kslot(FalseT{}));
+  phase_barrier();
+  if (n_masked > 0) apply_mask((nt - 1) * BN);
+  softmax();
+
+  // steady state: iteration i consumes V_i and K_{i+1}, loads V_{i+1}, K_{i+2}
+  // PAR is the parity of i: V_i and K_{i+2} live in slot PAR, K_{i+1} and
+  // V_{i+1} in the other one
+  auto iteration = [&](int i, auto par) {
+    constexpr bool PAR = decltype(par)::value;
+    typedef typename Bool<!PAR>::type Other;
+    sync_tile();  // V_i, K_{i+1} landed; every wave is done with V_{i-1}, K_i
+    if (grp == 0) {
+      if (i + 1 < nt) issue(rv, false, vslot(Other{}), i + 1);
+      if (i + 2 < nt) issue(rk, true, kslot(par), i + 2);
+    }
+    mfma_phase((const LDS_AS char*)vslot(par), kslot(Other{}), TrueT{});
+    phase_barrier();
+    if (i + 1 < n_masked) apply_mask((nt - 2 - i) * BN);
+    softmax();
+  };
+  // unrolled by two (the trip count is uniform over the workgroup), which
+  // also makes every slot index a compile-time constant
+  int i = 0;
+  for (; i + 1 < nt - 1; i += 2) {
+    iteration(i, FalseT{});
+    iteration(i + 1, TrueT{});
+  }
+  if (i < nt - 1) iteration(i, FalseT{});
+  // drain: the last tile's P V
+  sync_tile();
+  if ((nt - 1) & 1)
+    mfma_phase((const LDS_AS char*)vslot(TrueT{}), nullptr, FalseT{});
+  else
+    mfma_phase((const LDS_AS char*)vslot(FalseT{}), nullptr, FalseT{});
+  if (PP && grp == 0) barrier();
 
   // ---- finalize and epilogue ------------------------------------------------
   T* obase = (T*)a.o + head_off;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = halves_sum(l_run[qb]);
+    const float ll = halves_sum(l_lse[qb]);
     const bool ok = lt > 0.f;  // false for 0 and NaN
     const float inv = ok ? 1.0f / lt : 0.f;
     const int qi = qw + qb * 32 + l32;
     if (qi < N) {
       if (h32 == 0) {
-        const float lse = ok ? (m_run[qb] * c + __builtin_amdgcn_logf(lt)) * kLn2 : -__builtin_inff();
+        const float lse = ok ? (m_run[qb] * c + __builtin_amdgcn_logf(ll)) * kLn2 : -__builtin_inff();
         a.lse[(int64_t)bh * N + qi] = lse;
       }
       T* orow = obase + (int64_t)qi * a.H * D;
@@ -374,23 +525,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(KernelArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, int QB, int KB, bool CAUSAL, typename T>
+template <int D, int QB, int KB, bool CAUSAL, bool PP, typename T>
 int launch(const FwdArgs& f, hipStream_t st) {
-  constexpr int BM = 128 * QB;
+  constexpr int BM = (PP ? 256 : 128) * QB;
   KernelArgs a;
   a.q = f.q; a.k = f.k; a.v = f.v; a.o = f.o; a.lse = f.lse;
   a.B = f.B; a.H = f.H; a.N = f.N;
   a.n_mblk = (f.N + BM - 1) / BM;
   a.c = f.scale_log2;
   const int grid = a.n_mblk * f.B * f.H;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, KB, CAUSAL, T>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<D, QB, KB, CAUSAL, PP, T>), dim3(grid), dim3(PP ? 512 : 256), 0, st, a);
   return (int)hipGetLastError();
 }
 
 // Tile configuration per head dimension: QB = 32-row query blocks per wave,
 // KB = 32-key blocks per KV tile.
 #ifndef ATTN_D64_QB
-#define ATTN_D64_QB 2
+#define ATTN_D64_QB 1
 #endif
 #ifndef ATTN_D64_KB
 #define ATTN_D64_KB 2
@@ -399,7 +550,16 @@ int launch(const FwdArgs& f, hipStream_t st) {
 #define ATTN_D128_QB 1
 #endif
 #ifndef ATTN_D128_KB
-#define ATTN_D128_KB 2
+#define ATTN_D128_KB 1
+#endif
+#ifndef ATTN_D64_PP
+#define ATTN_D64_PP 1
+#endif
+#ifndef ATTN_D128_PP
+#define ATTN_D128_PP 0
+#endif
+#ifndef ATTN_D256_PP
+#define ATTN_D256_PP 0
 #endif
 #ifndef ATTN_D256_QB
 #define ATTN_D256_QB 1
@@ -412,7 +572,8 @@ template <int D, typename T>
 int dispatch_d(const FwdArgs& f, hipStream_t st) {
   constexpr int QB = D == 64 ? ATTN_D64_QB : D == 128 ? ATTN_D128_QB : ATTN_D256_QB;
   constexpr int KB = D == 64 ? ATTN_D64_KB : D == 128 ? ATTN_D128_KB : ATTN_D256_KB;
-  return f.causal ? launch<D, QB, KB, true, T>(f, st) : launch<D, QB, KB, false, T>(f, st);
+  constexpr bool PP = D == 64 ? ATTN_D64_PP : D == 128 ? ATTN_D128_PP : ATTN_D256_PP;
+  return f.causal ? launch<D, QB, KB, true, PP, T>(f, st) : launch<D, QB, KB, false, PP, T>(f, st);
 }
 
 template <typename T>

@@ -29,6 +29,14 @@ struct TrueT {
 struct FalseT {
   static constexpr bool value = false;
 };
+template <bool B>
+struct Bool {
+  typedef FalseT type;
+};
+template <>
+struct Bool<true> {
+  typedef TrueT type;
+};
 
 // s_waitcnt with only the vector-memory counter constrained (<= N in flight).
 template <int N>
