@@ -123,6 +123,15 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
 }
 
+#ifndef ATTN_STAGES
+#define ATTN_STAGES 2
+#endif
+#ifndef ATTN_LDS_PAD
+#define ATTN_LDS_PAD 0
+#endif
+#ifndef ATTN_SETPRIO
+#define ATTN_SETPRIO 0
+#endif
 #ifndef ATTN_LAZY_RESCALE
 #define ATTN_LAZY_RESCALE 1
 #endif
@@ -164,13 +173,23 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   constexpr int DB = D / 32;          // 32-dim blocks of O
   constexpr int DBL = DB < 4 ? DB : 4;
 
-  // Two K slots and two V slots, each its own object: slot choice is a
-  // compile-time parity below, so the compiler can see that a copy into one
-  // slot never aliases reads of another and need not serialise them.
+  // NS K slots and NS V slots, each its own object: slot choice is a
+  // compile-time constant below (the loop is unrolled by NS), so the
+  // compiler can see that a copy into one slot never aliases reads of
+  // another and need not serialise them.
+  constexpr int NS = ATTN_STAGES;
+  static_assert(NS == 2 || NS == 3, "2 or 3 LDS stages");
   __shared__ __attribute__((aligned(1024))) char kbuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf2[NS > 2 ? G::TILE : 1];
   __shared__ __attribute__((aligned(1024))) char vbuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf2[NS > 2 ? G::TILE : 1];
+#if ATTN_LDS_PAD
+  // extra LDS only to cap the number of resident workgroups per CU
+  __shared__ char ldspad[ATTN_LDS_PAD];
+  if (threadIdx.x == 1u << 30) ldspad[0] = 0;
+#endif
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -272,10 +291,17 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   }
   const int n_masked = max(0, nt - jm);
 
-  // LDS: two K slots then two V slots. K runs one tile ahead of V: while
-  // tile i's V and tile i+1's K are read, tile i+1's V and tile i+2's K load.
-  auto kslot = [&](auto par) -> char* { return decltype(par)::value ? kbuf1 : kbuf0; };
-  auto vslot = [&](auto par) -> char* { return decltype(par)::value ? vbuf1 : vbuf0; };
+  // LDS ring of NS stages; K runs one tile ahead of V. While tile i's V and
+  // tile i+1's K are read, tile i+NS-1's V and tile i+NS's K load. Tile j
+  // lives in slot j % NS (slot indices are compile-time constants).
+  auto kslot = [&](auto j) -> char* {
+    constexpr int J = decltype(j)::value % NS;
+    return J == 0 ? kbuf0 : J == 1 ? kbuf1 : kbuf2;
+  };
+  auto vslot = [&](auto j) -> char* {
+    constexpr int J = decltype(j)::value % NS;
+    return J == 0 ? vbuf0 : J == 1 ? vbuf1 : vbuf2;
+  };
   // Copy tile i (in processing order) of K or V into dst. The row offset of
   // segment t is the per-lane base plus a uniform stride; the base goes
   // through an empty asm so the compiler cannot hoist one VGPR per
@@ -302,8 +328,15 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   };
   // Start of a tile's MFMA phase: the copies group 0 issued two phases ago
   // have landed (its own wait, then the barrier publishes them).
-  auto sync_tile = [&]() {
-    if (grp == 0) wait_vmcnt<0>();
+  // Before iteration i (tile i's V, tile i+1's K): the copies issued after
+  // those two -- by the NS-2 iterations before i -- may stay in flight.
+  auto sync_tile = [&](int i) {
+    if (grp == 0) {
+      int later = 0;
+#pragma unroll
+      for (int t = 1; t <= NS - 2; ++t) later += (i + t < nt) + (i + t + 1 < nt);
+      wait_vmcnt_upto15(later * G::SEG_PER_WAVE);
+    }
     barrier();
   };
   auto phase_barrier = [&]() {
@@ -333,6 +366,7 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   // overlap: GEMM1 of tile i and GEMM0 of tile i+1 are independent).
   auto mfma_phase = [&](const LDS_AS char* vt, const char* kt, auto do_qk_tag) {
     constexpr bool DO_QK = decltype(do_qk_tag)::value;
+    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
     // O^T += V^T P^T first (P dies), then S^T = K Q^T (S is born): the two
     // never need registers at the same time
     constexpr int STEPS = DB * KB * 2;  // == KC * KB
@@ -363,6 +397,7 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   // Online softmax of the scores in s (tile starting at key kv0): running
@@ -450,48 +485,54 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   // group 0's by one; group 0 takes one extra at the end to match the count.
   if (PP && grp == 1) barrier();
 
-  // prologue: K and V of tile 0, K of tile 1; S and P of tile 0
+  // prologue: K_0, V_0, K_1, then V_t, K_{t+1} for t < NS-1; S and P of tile 0
   if (grp == 0) {
-    issue(rk, true, kslot(FalseT{}), 0);
-    issue(rv, false, vslot(FalseT{}), 0);
-    if (nt > 1) issue(rk, true, kslot(TrueT{}), 1);
+    issue(rk, true, kslot(Int<0>{}), 0);
+    issue(rv, false, vslot(Int<0>{}), 0);
+    if (nt > 1) issue(rk, true, kslot(Int<1>{}), 1);
+    if (NS > 2) {
+      if (nt > 1) issue(rv, false, vslot(Int<1>{}), 1);
+      if (nt > 2) issue(rk, true, kslot(Int<2>{}), 2);
+    }
+    wait_vmcnt<0>();
   }
-  sync_tile();
-  qk(kslot(FalseT{}));
+  barrier();
+  qk(kslot(Int<0>{}));
   phase_barrier();
   if (n_masked > 0) apply_mask((nt - 1) * BN);
   softmax();
 
-  // steady state: iteration i consumes V_i and K_{i+1}, loads V_{i+1}, K_{i+2}
-  // PAR is the parity of i: V_i and K_{i+2} live in slot PAR, K_{i+1} and
-  // V_{i+1} in the other one
-  auto iteration = [&](int i, auto par) {
-    constexpr bool PAR = decltype(par)::value;
-    typedef typename Bool<!PAR>::type Other;
-    sync_tile();  // V_i, K_{i+1} landed; every wave is done with V_{i-1}, K_i
+  // steady state: iteration i (slot phase J = i % NS) consumes V_i and
+  // K_{i+1}, loads V_{i+NS-1} and K_{i+NS}
+  auto iteration = [&](int i, auto jtag) {
+    constexpr int J = decltype(jtag)::value;
+    sync_tile(i);  // V_i, K_{i+1} landed; every wave is done with V_{i-1}, K_i
     if (grp == 0) {
-      if (i + 1 < nt) issue(rv, false, vslot(Other{}), i + 1);
-      if (i + 2 < nt) issue(rk, true, kslot(par), i + 2);
+      if (i + NS - 1 < nt) issue(rv, false, vslot(Int<J + NS - 1>{}), i + NS - 1);
+      if (i + NS < nt) issue(rk, true, kslot(Int<J + NS>{}), i + NS);
     }
-    mfma_phase((const LDS_AS char*)vslot(par), kslot(Other{}), TrueT{});
+    mfma_phase((const LDS_AS char*)vslot(Int<J>{}), kslot(Int<J + 1>{}), TrueT{});
     phase_barrier();
     if (i + 1 < n_masked) apply_mask((nt - 2 - i) * BN);
     softmax();
   };
-  // unrolled by two (the trip count is uniform over the workgroup), which
-  // also makes every slot index a compile-time constant
+  // unrolled by NS (the trip count is uniform over the workgroup), which
+  // makes every slot index a compile-time constant
   int i = 0;
-  for (; i + 1 < nt - 1; i += 2) {
-    iteration(i, FalseT{});
-    iteration(i + 1, TrueT{});
+  for (; i + NS - 1 < nt - 1; i += NS) {
+    iteration(i, Int<0>{});
+    iteration(i + 1, Int<1>{});
+    if (NS > 2) iteration(i + 2, Int<2>{});
   }
-  if (i < nt - 1) iteration(i, FalseT{});
+  if (i < nt - 1) iteration(i, Int<0>{});
+  if (NS > 2 && i + 1 < nt - 1) iteration(i + 1, Int<1>{});
   // drain: the last tile's P V
-  sync_tile();
-  if ((nt - 1) & 1)
-    mfma_phase((const LDS_AS char*)vslot(TrueT{}), nullptr, FalseT{});
-  else
-    mfma_phase((const LDS_AS char*)vslot(FalseT{}), nullptr, FalseT{});
+  sync_tile(nt - 1);
+  switch ((nt - 1) % NS) {
+    case 0: mfma_phase((const LDS_AS char*)vslot(Int<0>{}), nullptr, FalseT{}); break;
+    case 1: mfma_phase((const LDS_AS char*)vslot(Int<1>{}), nullptr, FalseT{}); break;
+    default: mfma_phase((const LDS_AS char*)vslot(Int<2>{}), nullptr, FalseT{}); break;
+  }
   if (PP && grp == 0) barrier();
 
   // ---- finalize and epilogue ------------------------------------------------
@@ -553,7 +594,7 @@ int launch(const FwdArgs& f, hipStream_t st) {
 #define ATTN_D128_KB 1
 #endif
 #ifndef ATTN_D64_PP
-#define ATTN_D64_PP 1
+#define ATTN_D64_PP 0
 #endif
 #ifndef ATTN_D128_PP
 #define ATTN_D128_PP 0
