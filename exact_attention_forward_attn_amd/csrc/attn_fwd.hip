@@ -63,15 +63,16 @@ struct Elt<__bf16> {
   static __device__ __forceinline__ v4 tr_read(const LDS_AS char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4*)p);
   }
-  // acc + sum of the eight 16-bit values (v_dot2 against (1, 1), fp32 sum)
-  static __device__ __forceinline__ float sum8(v8 x, float acc) {
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    struct P4 { b2 p[4]; };
-    const P4 pr = __builtin_bit_cast(P4, x);
-    const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(pr.p[i], one, acc, false);
-    return acc;
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  // two floats rounded (to nearest even) to one packed 16-bit pair
+  static __device__ __forceinline__ v2 cvt2(float a, float b) {
+    const float __attribute__((ext_vector_type(2))) f = {a, b};
+    return __builtin_convertvector(f, v2);
+  }
+  // acc + x.x + x.y, summed in float32 (v_dot2 against (1, 1))
+  static __device__ __forceinline__ float dot2(v2 x, float acc) {
+    const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
   }
 };
 
@@ -86,14 +87,14 @@ struct Elt<_Float16> {
   static __device__ __forceinline__ v4 tr_read(const LDS_AS char* p) {
     return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS raw4*)p));
   }
-  static __device__ __forceinline__ float sum8(v8 x, float acc) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    struct P4 { h2 p[4]; };
-    const P4 pr = __builtin_bit_cast(P4, x);
-    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(pr.p[i], one, acc, false);
-    return acc;
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ v2 cvt2(float a, float b) {
+    const float __attribute__((ext_vector_type(2))) f = {a, b};
+    return __builtin_convertvector(f, v2);
+  }
+  static __device__ __forceinline__ float dot2(v2 x, float acc) {
+    const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(x, one, acc, false);
   }
 };
 
@@ -123,26 +124,11 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
 }
 
-#ifndef ATTN_STAGES
-#define ATTN_STAGES 2
-#endif
-#ifndef ATTN_LDS_PAD
-#define ATTN_LDS_PAD 0
-#endif
-#ifndef ATTN_SETPRIO
-#define ATTN_SETPRIO 0
-#endif
-#ifndef ATTN_LAZY_RESCALE
-#define ATTN_LAZY_RESCALE 1
+#ifndef ATTN_DS_LEAD
+#define ATTN_DS_LEAD 2
 #endif
 // rescale threshold of the lazy path, in base-2 exponent units
 constexpr float kTau = 8.0f;
-#ifndef ATTN_SB_K
-#define ATTN_SB_K 4
-#endif
-#ifndef ATTN_SB_V
-#define ATTN_SB_V 2
-#endif
 
 struct KernelArgs {
   const void* q;
@@ -155,50 +141,74 @@ struct KernelArgs {
   float c;        // alpha * log2(e)
 };
 
-template <int D, int QB, int KB, bool CAUSAL, bool PP, typename T>
-__global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
+// Lambdas of the kernels are always inlined (their captures must stay in
+// registers).
+#define ATTN_INLINE __attribute__((always_inline))
+
+// Empty asm that takes x in VGPRs and may change it: the computation of x
+// cannot move past this point, which keeps work inside its pipeline step.
+template <typename X>
+__device__ __forceinline__ void pin(X& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Compile-time loop: f(Int<u>) for u = B .. E-1.
+template <int B, int E>
+struct For {
+  template <typename F>
+  static __device__ __forceinline__ void run(F&& f) {
+    if constexpr (B < E) {
+      f(Int<B>{});
+      For<B + 1, E>::run(f);
+    }
+  }
+};
+
+// Software pipeline of one wave (tile i = i-th KV tile in processing order):
+//
+//   block i:  S_{i+2}^T = K_{i+2} Q^T  (MFMA)
+//             O^T += V_i^T P_i^T       (MFMA)
+//             P_{i+1} from S_{i+1}     (VALU, in the MFMA shadow)
+//
+// The three parts are independent, so the VALU work of the softmax issues
+// while the matrix core runs the two products (the pages overlap the softmax
+// of one block with the GEMMs of others, "FlashAttention-3 on Hopper",
+// sections 3.4.2 and 4.5). S and P are double-buffered in registers by tile
+// parity.
+//
+// LDS holds two K and two V tiles. K runs two tiles ahead of V: block i
+// reads V_i and K_{i+2} while V_{i+1} and K_{i+3} are copied in.
+template <int D, int KB, bool CAUSAL, typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+void fwd_kernel(KernelArgs a) {
   // The body is device code only; the host pass just needs the launch stub
   // (instantiating the body there makes clang drop the stub silently).
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef Elt<T> E;
   typedef typename E::v8 v8;
   typedef typename E::v4 v4;
+  typedef typename E::v2 v2;
   typedef Geo<D, KB> G;
   constexpr int BN = G::BN;
-  constexpr int WQ = 32 * QB;         // query rows per wave
-  constexpr int WAVES = PP ? 8 : 4;   // ping-pong: two groups of four waves
-  constexpr int BM = WAVES * WQ;      // query rows per workgroup
+  constexpr int BM = 128;             // query rows per workgroup (32 per wave)
   constexpr int KC = D / 16;          // k-steps of the QK^T product
   constexpr int KCL = KC < 8 ? KC : 8;
   constexpr int DB = D / 32;          // 32-dim blocks of O
   constexpr int DBL = DB < 4 ? DB : 4;
 
-  // NS K slots and NS V slots, each its own object: slot choice is a
-  // compile-time constant below (the loop is unrolled by NS), so the
-  // compiler can see that a copy into one slot never aliases reads of
-  // another and need not serialise them.
-  constexpr int NS = ATTN_STAGES;
-  static_assert(NS == 2 || NS == 3, "2 or 3 LDS stages");
+  // Each slot is its own object and every slot index below is a compile-time
+  // constant (the loop is unrolled by two), so the compiler can see that a
+  // copy into one slot never aliases reads of another and need not serialise
+  // them.
   __shared__ __attribute__((aligned(1024))) char kbuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char kbuf1[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char kbuf2[NS > 2 ? G::TILE : 1];
   __shared__ __attribute__((aligned(1024))) char vbuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char vbuf1[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char vbuf2[NS > 2 ? G::TILE : 1];
-#if ATTN_LDS_PAD
-  // extra LDS only to cap the number of resident workgroups per CU
-  __shared__ char ldspad[ATTN_LDS_PAD];
-  if (threadIdx.x == 1u << 30) ldspad[0] = 0;
-#endif
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h32 = lane >> 5;   // which half of the wave
   const int l32 = lane & 31;
-  // Group 0 (waves 0-3) issues every K/V copy; with ping-pong, group 1
-  // (waves 4-7) runs one phase behind it.
-  const int grp = PP ? (wave >> 2) : 0;
-  const int lw = wave & 3;     // wave index within its group (copy segments)
 
   // ---- work decomposition -------------------------------------------------
   const int BH = a.B * a.H;
@@ -208,7 +218,8 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   const int hh = bh % a.H;
   const int N = a.N;
   const int q0 = mblk * BM;
-  const int qw = q0 + wave * WQ;              // first query row of this wave
+  const int qw = q0 + wave * 32;              // first query row of this wave
+  const int qi = qw + l32;                    // this lane's query row
   const uint32_t RS = (uint32_t)a.H * D * 2;  // bytes between consecutive rows
   const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;  // elements
   const uint32_t span = (uint32_t)(N - 1) * RS + D * 2;       // valid bytes of this head
@@ -218,33 +229,29 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + head_off, span);
 
   // ---- Q^T operands (B operand of S^T = K Q^T), resident in VGPRs ----------
-  v8 qreg[QB][KC];
+  v8 qreg[KC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const uint32_t row = (uint32_t)(qw + qb * 32 + l32);
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rq, row * RS + (16 * kc + 8 * h32) * 2, 0, 0);
-      qreg[qb][kc] = __builtin_bit_cast(v8, raw);
-    }
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qi * RS + (16 * kc + 8 * h32) * 2, 0, 0);
+    qreg[kc] = __builtin_bit_cast(v8, raw);
   }
 
   // ---- per-lane LDS offsets -------------------------------------------------
-  // global -> LDS copy: segment seg = lw + 4t, lane i covers row seg*RPS + i/CPR,
-  // chunk i%CPR. The swizzles depend on the row modulo 16 (K) or 4 (V); a step
-  // of t moves the row by 4*RPS, which keeps both except for K rows of 512
-  // bytes (RPS = 2), where the parity of t matters. So one per-lane base
+  // global -> LDS copy: segment seg = wave + 4t, lane i covers row seg*RPS +
+  // i/CPR, chunk i%CPR. The swizzles depend on the row modulo 16 (K) or 4 (V);
+  // a step of t moves the row by 4*RPS, which keeps both except for K rows of
+  // 512 bytes (RPS = 2), where the parity of t matters. So one per-lane base
   // (two for that K case) plus a uniform per-segment stride covers all t.
   constexpr int KGP = (G::RPS * 4) % 16 == 0 ? 1 : 2;
   uint32_t kg[KGP], vg0;
 #pragma unroll
   for (int t = 0; t < KGP; ++t) {
-    const int r = (lw + 4 * t) * G::RPS + lane / G::CPR;
+    const int r = (wave + 4 * t) * G::RPS + lane / G::CPR;
     const int pc = lane % G::CPR;
     kg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * 4 * G::RPS * RS;
   }
   {
-    const int r = lw * G::RPS + lane / G::CPR;
+    const int r = wave * G::RPS + lane / G::CPR;
     const int pc = lane % G::CPR;
     vg0 = (uint32_t)r * RS + (uint32_t)((pc ^ swz_v<D>(r)) << 4);
   }
@@ -265,19 +272,17 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   }
 
   // ---- online softmax state -------------------------------------------------
-  f32x16 oacc[QB][DB];
-  // m_run: running max (the exponent reference); l_run: sum of the rounded P
-  // that entered P V (normalises O); l_lse: float32 sum of P (gives LSE)
-  float m_run[QB], l_run[QB], l_lse[QB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -__builtin_inff();
-    l_run[qb] = 0.f;
-    l_lse[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
-  }
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   const float c = a.c;
+  const float tau_c = kTau / c;
+  // m_run: the exponent reference (a running max); msc = m_run * c (0 while
+  // m_run = -inf); thr = m_run + kTau / c, the largest score it covers.
+  // l_run: sum of the rounded P that entered P V (normalises O); l_lse:
+  // float32 sum of P (gives LSE).
+  float m_run = -__builtin_inff(), msc = 0.f, thr = -__builtin_inff();
+  float l_run = 0.f, l_lse = 0.f;
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;
@@ -291,22 +296,14 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
   }
   const int n_masked = max(0, nt - jm);
 
-  // LDS ring of NS stages; K runs one tile ahead of V. While tile i's V and
-  // tile i+1's K are read, tile i+NS-1's V and tile i+NS's K load. Tile j
-  // lives in slot j % NS (slot indices are compile-time constants).
-  auto kslot = [&](auto j) -> char* {
-    constexpr int J = decltype(j)::value % NS;
-    return J == 0 ? kbuf0 : J == 1 ? kbuf1 : kbuf2;
-  };
-  auto vslot = [&](auto j) -> char* {
-    constexpr int J = decltype(j)::value % NS;
-    return J == 0 ? vbuf0 : J == 1 ? vbuf1 : vbuf2;
-  };
+  // Tile i (processing order) lives in slot i % 2.
+  auto kslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? kbuf1 : kbuf0; };
+  auto vslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? vbuf1 : vbuf0; };
   // Copy tile i (in processing order) of K or V into dst. The row offset of
   // segment t is the per-lane base plus a uniform stride; the base goes
   // through an empty asm so the compiler cannot hoist one VGPR per
   // (slot, segment) out of the loop.
-  auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) {
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) ATTN_INLINE {
     const uint32_t base = (uint32_t)((nt - 1 - i) * BN) * RS;
     uint32_t g0 = is_k ? kg[0] : vg0;
     uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
@@ -314,296 +311,313 @@ __global__ __launch_bounds__(PP ? 512 : 256) void fwd_kernel(KernelArgs a) {
 #pragma unroll
     for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
       const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * 4 * G::RPS * RS);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (lw + 4 * t) * 1024), 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + 4 * t) * 1024), 16, voff, 0, 0, 0);
     }
   };
-  // Workgroup barrier at a phase boundary. Every LDS read of this wave has
-  // landed first (the compiler may otherwise sink the barrier above a pending
-  // ds_read), and no work crosses it in either direction.
-  auto barrier = [&]() {
+  // Workgroup barrier. Every LDS read of this wave has landed first (the
+  // compiler may otherwise sink the barrier above a pending ds_read), and no
+  // work crosses it in either direction.
+  auto barrier = [&]() ATTN_INLINE {
     wait_lgkmcnt0();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Start of a tile's MFMA phase: the copies group 0 issued two phases ago
-  // have landed (its own wait, then the barrier publishes them).
-  // Before iteration i (tile i's V, tile i+1's K): the copies issued after
-  // those two -- by the NS-2 iterations before i -- may stay in flight.
-  auto sync_tile = [&](int i) {
-    if (grp == 0) {
-      int later = 0;
-#pragma unroll
-      for (int t = 1; t <= NS - 2; ++t) later += (i + t < nt) + (i + t + 1 < nt);
-      wait_vmcnt_upto15(later * G::SEG_PER_WAVE);
-    }
-    barrier();
-  };
-  auto phase_barrier = [&]() {
-    if (PP) barrier();
-  };
 
-  f32x16 s[KB][QB];
-  v8 pk[KB][QB][2];
+  f32x16 s[2][KB];   // S^T of two tiles (index: tile parity)
+  v8 pk[2][KB][2];   // P of two tiles, 16-bit, as MFMA B operands
 
-  // S^T = K Q^T for one tile (QK only: the prologue)
-  auto qk = [&](const char* kt) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+  // S^T = K Q^T of one tile into s[SB] (prologue only)
+  auto qk = [&](auto sb_tag, const char* kt) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
 #pragma unroll
     for (int t = 0; t < KC * KB; ++t) {
       const int kc = t / KB, kb = t % KB;
       const v8 ka = *(const v8*)(kt + kb * 32 * G::ROWB + (kc / 8) * 256 + kofs[kc % 8]);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma(ka, qreg[qb][kc], s[kb][qb]);
+      s[SB][kb] = E::mfma(ka, qreg[kc], kc == 0 ? f32x16{} : s[SB][kb]);
     }
   };
 
-  // The MFMA phase of one iteration: O^T += V^T P^T for the current tile,
-  // interleaved with S^T = K Q^T for the next one (the pages' intra-warpgroup
-  // overlap: GEMM1 of tile i and GEMM0 of tile i+1 are independent).
-  auto mfma_phase = [&](const LDS_AS char* vt, const char* kt, auto do_qk_tag) {
-    constexpr bool DO_QK = decltype(do_qk_tag)::value;
-    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-    // O^T += V^T P^T first (P dies), then S^T = K Q^T (S is born): the two
-    // never need registers at the same time
-    constexpr int STEPS = DB * KB * 2;  // == KC * KB
-#pragma unroll
-    for (int t = 0; t < STEPS; ++t) {
-      if (t % ATTN_SB_V == 0) __builtin_amdgcn_sched_barrier(0);
-      const int db = t / (2 * KB), kb = (t / 2) % KB, ks = t % 2;
-      const LDS_AS char* pv = vt + (kb * 32 + 16 * ks) * G::ROWB + (db / 4) * 256 + vofs[db % 4];
-      const v4 lo = E::tr_read(pv);
-      const v4 hi = E::tr_read(pv + 8 * G::ROWB);
-      const v8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(va, pk[kb][qb][ks], oacc[qb][db]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (DO_QK) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int t = 0; t < KC * KB; ++t) {
-        if (t % ATTN_SB_K == 0) __builtin_amdgcn_sched_barrier(0);
-        const int kc = t / KB, kb = t % KB;
-        const v8 ka = *(const v8*)(kt + kb * 32 * G::ROWB + (kc / 8) * 256 + kofs[kc % 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = E::mfma(ka, qreg[qb][kc], s[kb][qb]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-  };
-
-  // Online softmax of the scores in s (tile starting at key kv0): running
-  // max, P = 2^(s c - m c) packed to 16 bits in pk, l, and the O rescale.
   // Scores of keys past N or right of the diagonal become -inf (only the
-  // tiles of the masked prefix call this).
-  auto apply_mask = [&](int kv0) {
+  // tiles of the masked prefix call this). kv0: first key of the tile.
+  auto apply_mask = [&](auto sb_tag, int kv0) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
     // key offset within the tile = 4*h32 + o with o a compile-time constant,
     // so compare o against per-lane thresholds (no per-element index vectors)
-    const int tn = N - kv0 - 4 * h32;  // o >= tn: key at or past N
+    const int tn = N - kv0 - 4 * h32;          // o >= tn: key at or past N
+    const int tc = qi - kv0 - 4 * h32;         // o > tc: key right of the diagonal
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int tc = qw + qb * 32 + l32 - kv0 - 4 * h32;  // o > tc: key right of the diagonal
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
-          if (o >= tn || (CAUSAL && o > tc)) s[kb][qb][r] = -__builtin_inff();
-        }
-    }
-  };
-
-  auto softmax = [&]() {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][qb][r]);
-      mx = halves_max(mx);
-#if ATTN_LAZY_RESCALE
-      // Conditional rescale ("FlashAttention v1-v4", FA4 section): m_run is
-      // the reference the exponents are taken against. It only moves when
-      // some row's maximum exceeds it by more than kTau base-2 units, so
-      // p <= 2^kTau, and O~ and l are rescaled only then. O = O~/l and
-      // LSE = m c + log2 l are unchanged in exact arithmetic.
-      const float mref = m_run[qb];
-      if (__builtin_amdgcn_ballot_w64((mx - mref) * c > kTau) != 0) {
-        const float m_new = __builtin_fmaxf(mref, mx);
-        const float rho = (m_new == -__builtin_inff()) ? 1.f : exp2_fast((mref - m_new) * c);
-        m_run[qb] = m_new;
-        l_run[qb] *= rho;
-        l_lse[qb] *= rho;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[qb][db] *= rho;
+      for (int r = 0; r < 16; ++r) {
+        const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
+        if (o >= tn || (CAUSAL && o > tc)) s[SB][kb][r] = -__builtin_inff();
       }
-      const float ms = (m_run[qb] == -__builtin_inff()) ? 0.f : m_run[qb] * c;
-#else
-      const float m_new = __builtin_fmaxf(m_run[qb], mx);
-      const float ms = (m_new == -__builtin_inff()) ? 0.f : m_new * c;
-      const float rho = exp2_fast(m_run[qb] * c - ms);
-      m_run[qb] = m_new;
-      l_run[qb] *= rho;
-      l_lse[qb] *= rho;
-#endif
-      // P = 2^(s c - m c), rounded to 16 bits in place: these registers are
-      // the B operand of the next P V product. l sums the rounded values, so
-      // O~/l is an exact convex combination of the weights the product used.
-      float rs = 0.f, rs32 = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          f32x8 f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            f[e] = exp2_fast(__builtin_fmaf(s[kb][qb][8 * ks + e], c, -ms));
-            rs32 += f[e];
-          }
-          pk[kb][qb][ks] = __builtin_convertvector(f, v8);
-          rs = E::sum8(pk[kb][qb][ks], rs);
+  };
+
+  // ---- online softmax of one tile -------------------------------------------
+  // Conditional rescale ("FlashAttention v1-v4", FA4 section): the exponent
+  // reference m_run moves only when some row's maximum exceeds it by more
+  // than kTau base-2 units, so every p = 2^(s c - m_run c) <= 2^kTau. A tile
+  // therefore nearly always keeps the current reference, and P is computed
+  // against it right away while an independent max tree checks the rule; a
+  // tile that breaks it (the first one always does) is redone after its
+  // block against the new reference, and O~ and l are multiplied by
+  // rho = 2^((m_old - m_new) c). O = O~/l and LSE = m c + log2 l are
+  // unchanged in exact arithmetic. l_run sums the rounded p that enter P V,
+  // so O~/l_run is an exact convex combination of the weights the product
+  // used; l_lse is the float32 sum (gives the LSE).
+  //
+  // The work is cut into single VALU instructions placed on the steps of a
+  // block (one MFMA each) so that no instruction waits on the one just
+  // before it: score e has its fma at step f(e), its exp at f(e)+1, its
+  // float32 add and 16-bit pack at f(e)+2, the pack's dot2 at f(e)+3. Sums
+  // and maxima use two independent partials each.
+  constexpr int NV = 16 * KB;  // scores per lane in a tile
+  float fv[NV];
+  float pmx[2], mxv, r32p[2], r16p[2], r32v, r16v;
+  v2 pp[NV / 2];
+  bool need = false;
+
+  // The step schedule of a block of M MFMA steps.
+  struct Sched {
+    int M;
+    constexpr int span() const { return M > 4 ? M - 3 : 1; }
+    constexpr int f(int e) const { return (e * span()) / NV; }
+    constexpr int maxs() const { return (M / 2 < NV / 4 ? M / 2 : NV / 4) > 0 ? (M / 2 < NV / 4 ? M / 2 : NV / 4) : 1; }
+    constexpr int last() const { return f(NV - 1) + 4 > maxs() + 1 ? f(NV - 1) + 4 : maxs() + 1; }
+  };
+
+  // VALU work of step k (on the M-step schedule) for the tile in s[SB].
+  // WITH_MAX adds the max tree and the check of the reference.
+  auto sm_step = [&](auto sb_tag, auto k_tag, auto m_tag, auto max_tag) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
+    constexpr int K = decltype(k_tag)::value;
+    constexpr Sched S{decltype(m_tag)::value};
+    constexpr bool WITH_MAX = decltype(max_tag)::value;
+    constexpr int CH = NV / S.maxs();  // scores per max step
+    For<0, NV>::run([&](auto e_tag) ATTN_INLINE {
+      constexpr int e = decltype(e_tag)::value;
+      constexpr int f = S.f(e);
+      // row max: pairs of scores folded into two partials (v_max3)
+      if constexpr (WITH_MAX && e % 2 == 0 && e / CH == K) {
+        constexpr int j = ((e % CH) / 2) % 2;
+        const float x0 = s[SB][e / 16][e % 16], x1 = s[SB][(e + 1) / 16][(e + 1) % 16];
+        pmx[j] = (e < 4) ? __builtin_fmaxf(x0, x1) : __builtin_fmaxf(__builtin_fmaxf(pmx[j], x0), x1);
+        pin(pmx[j]);
+      }
+      if constexpr (f == K) {
+        fv[e] = __builtin_fmaf(s[SB][e / 16][e % 16], c, -msc);
+        pin(fv[e]);
+      }
+      if constexpr (f + 1 == K) {
+        fv[e] = exp2_fast(fv[e]);
+        pin(fv[e]);
+      }
+      if constexpr (f + 2 == K) {
+        r32p[e % 2] = e < 2 ? fv[e] : r32p[e % 2] + fv[e];
+        pin(r32p[e % 2]);
+        if constexpr (e % 2 == 1) {
+          pp[e / 2] = E::cvt2(fv[e - 1], fv[e]);
+          pin(pp[e / 2]);
         }
-      l_run[qb] += rs;
-      l_lse[qb] += rs32;
-#if !ATTN_LAZY_RESCALE
+      }
+      if constexpr (e % 2 == 1 && f + 3 == K) {
+        constexpr int q = e / 2;
+        r16p[q % 2] = E::dot2(pp[q], q < 2 ? 0.f : r16p[q % 2]);
+        pin(r16p[q % 2]);
+      }
+    });
+    if constexpr (WITH_MAX && K == S.maxs()) {
+      mxv = __builtin_fmaxf(pmx[0], pmx[1]);
+      pin(mxv);
+    }
+    if constexpr (WITH_MAX && K == S.maxs() + 1) need = __builtin_amdgcn_ballot_w64(mxv > thr) != 0;
+    if constexpr (K == S.last()) {
+      r32v = r32p[0] + r32p[1];
+      r16v = r16p[0] + r16p[1];
+      // the packed pairs become the B operands of the tile's P V product
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[qb][db] *= rho;
-#endif
+      for (int g = 0; g < 2 * KB; ++g) {
+        struct P4 { v2 p[4]; };
+        const P4 t = {{pp[4 * g], pp[4 * g + 1], pp[4 * g + 2], pp[4 * g + 3]}};
+        pk[SB][g / 2][g % 2] = __builtin_bit_cast(v8, t);
+      }
     }
   };
-
-  // Ping-pong: group 1 takes one extra barrier first so its phases trail
-  // group 0's by one; group 0 takes one extra at the end to match the count.
-  if (PP && grp == 1) barrier();
-
-  // prologue: K_0, V_0, K_1, then V_t, K_{t+1} for t < NS-1; S and P of tile 0
-  if (grp == 0) {
-    issue(rk, true, kslot(Int<0>{}), 0);
-    issue(rv, false, vslot(Int<0>{}), 0);
-    if (nt > 1) issue(rk, true, kslot(Int<1>{}), 1);
-    if (NS > 2) {
-      if (nt > 1) issue(rv, false, vslot(Int<1>{}), 1);
-      if (nt > 2) issue(rk, true, kslot(Int<2>{}), 2);
+  // Close a tile's softmax after its block: the rare reference update (P
+  // redone against the new reference, O~ and l rescaled), then l.
+  auto finish_tile = [&](auto sb_tag) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
+    if (need) {
+      const float m_new = __builtin_fmaxf(m_run, halves_max(mxv));
+      const float rho = (m_new == -__builtin_inff()) ? 1.f : exp2_fast((m_run - m_new) * c);
+      m_run = m_new;
+      msc = (m_new == -__builtin_inff()) ? 0.f : m_new * c;
+      thr = m_new + tau_c;
+      constexpr Sched S1{1};
+      For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<SB>{}, k, Int<1>{}, FalseT{}); });
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= rho;
+      l_run *= rho;
+      l_lse *= rho;
     }
-    wait_vmcnt<0>();
-  }
+    l_run += r16v;
+    l_lse += r32v;
+  };
+
+  // Block i of the pipeline (J = i % 2): S_{i+2}^T = K_{i+2} Q^T into s[J]
+  // (the buffer S_i came from) and O^T += V_i^T P_i^T, one MFMA per step;
+  // each step also issues the LDS reads of the MFMA DS_LEAD steps later and
+  // its share of the softmax of S_{i+1}. Fences between the steps keep that
+  // order (the compiler would otherwise cluster the VALU work).
+  auto block = [&](auto j_tag, auto qk_tag, auto sm_tag) ATTN_INLINE {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr int SN = J ^ 1;
+    constexpr bool DO_QK = decltype(qk_tag)::value;
+    constexpr bool DO_SM = decltype(sm_tag)::value;
+    constexpr int MPV = DB * KB * 2;
+    constexpr int MQK = DO_QK ? KC * KB : 0;
+    constexpr int M = MPV + MQK;
+    constexpr Sched S{M};
+    constexpr int STEPS = DO_SM ? (S.last() + 1 > M ? S.last() + 1 : M) : M;
+    constexpr int LEAD = ATTN_DS_LEAD;
+    const LDS_AS char* vt = (const LDS_AS char*)vslot(Int<J>{});
+    const char* kt = kslot(Int<J>{});
+    // MFMA m: QK step (kc, kb) first, then PV step (db, kb, ks)
+    auto load_op = [&](auto m_tag) ATTN_INLINE -> v8 {
+      constexpr int m = decltype(m_tag)::value;
+      if constexpr (m < MQK) {
+        constexpr int kc = m / KB, kb = m % KB;
+        return *(const v8*)(kt + kb * 32 * G::ROWB + (kc / 8) * 256 + kofs[kc % 8]);
+      } else {
+        constexpr int t = m - MQK;
+        constexpr int db = t / (2 * KB), kb = (t / 2) % KB, ks = t % 2;
+        const LDS_AS char* p = vt + (kb * 32 + 16 * ks) * G::ROWB + (db / 4) * 256 + vofs[db % 4];
+        const v4 lo = E::tr_read(p);
+        const v4 hi = E::tr_read(p + 8 * G::ROWB);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    auto mfma_op = [&](auto m_tag, v8 op) ATTN_INLINE {
+      constexpr int m = decltype(m_tag)::value;
+      if constexpr (m < MQK) {
+        constexpr int kc = m / KB, kb = m % KB;
+        s[J][kb] = E::mfma(op, qreg[kc], kc == 0 ? f32x16{} : s[J][kb]);
+      } else {
+        constexpr int t = m - MQK;
+        constexpr int db = t / (2 * KB), kb = (t / 2) % KB, ks = t % 2;
+        oacc[db] = E::mfma(op, pk[J][kb][ks], oacc[db]);
+      }
+    };
+    v8 ring[LEAD];
+    For<0, (LEAD < M ? LEAD : M)>::run([&](auto m) ATTN_INLINE { ring[decltype(m)::value % LEAD] = load_op(m); });
+    For<0, STEPS>::run([&](auto k_tag) ATTN_INLINE {
+      constexpr int k = decltype(k_tag)::value;
+      if constexpr (k < M) {
+        mfma_op(k_tag, ring[k % LEAD]);
+        if constexpr (k + LEAD < M) ring[k % LEAD] = load_op(Int<k + LEAD>{});
+      }
+      if constexpr (DO_SM) sm_step(Int<SN>{}, k_tag, Int<M>{}, TrueT{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (DO_SM) finish_tile(Int<SN>{});
+  };
+
+  // prologue: K_0, K_1, V_0; S_0, S_1; P_0; then K_2 into K_0's slot
+  issue(rk, true, kbuf0, 0);
+  if (nt > 1) issue(rk, true, kbuf1, 1);
+  issue(rv, false, vbuf0, 0);
+  wait_vmcnt<0>();
   barrier();
-  qk(kslot(Int<0>{}));
-  phase_barrier();
-  if (n_masked > 0) apply_mask((nt - 1) * BN);
-  softmax();
+  qk(Int<0>{}, kbuf0);
+  if (nt > 1) qk(Int<1>{}, kbuf1);
+  barrier();  // every wave has read K_0
+  if (nt > 2) issue(rk, true, kbuf0, 2);
+  if (n_masked > 0) apply_mask(Int<0>{}, (nt - 1) * BN);
+  if (n_masked > 1) apply_mask(Int<1>{}, (nt - 2) * BN);
+  {
+    constexpr Sched S0{16};
+    For<0, S0.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<16>{}, TrueT{}); });
+    finish_tile(Int<0>{});
+  }
 
-  // steady state: iteration i (slot phase J = i % NS) consumes V_i and
-  // K_{i+1}, loads V_{i+NS-1} and K_{i+NS}
-  auto iteration = [&](int i, auto jtag) {
-    constexpr int J = decltype(jtag)::value;
-    sync_tile(i);  // V_i, K_{i+1} landed; every wave is done with V_{i-1}, K_i
-    if (grp == 0) {
-      if (i + NS - 1 < nt) issue(rv, false, vslot(Int<J + NS - 1>{}), i + NS - 1);
-      if (i + NS < nt) issue(rk, true, kslot(Int<J + NS>{}), i + NS);
-    }
-    mfma_phase((const LDS_AS char*)vslot(Int<J>{}), kslot(Int<J + 1>{}), TrueT{});
-    phase_barrier();
-    if (i + 1 < n_masked) apply_mask((nt - 2 - i) * BN);
-    softmax();
+  // iteration i: V_i and K_{i+2} have landed (copied during iteration i-1)
+  // and every wave is past block i-1, so the slots of V_{i-1} and K_{i+1}
+  // take V_{i+1} and K_{i+3}.
+  auto iteration = [&](int i, auto j_tag, auto qk_tag, auto sm_tag) ATTN_INLINE {
+    constexpr int J = decltype(j_tag)::value;
+    wait_vmcnt<0>();
+    barrier();
+    if (i + 1 < nt) issue(rv, false, vslot(Int<J + 1>{}), i + 1);
+    if (i + 3 < nt) issue(rk, true, kslot(Int<J + 1>{}), i + 3);
+    block(j_tag, qk_tag, sm_tag);
+    if (decltype(qk_tag)::value && i + 2 < n_masked) apply_mask(Int<J>{}, (nt - 3 - i) * BN);
   };
-  // unrolled by NS (the trip count is uniform over the workgroup), which
-  // makes every slot index a compile-time constant
+  // unrolled by two (the trip count is uniform over the workgroup), which
+  // makes every slot and buffer index a compile-time constant
   int i = 0;
-  for (; i + NS - 1 < nt - 1; i += NS) {
-    iteration(i, Int<0>{});
-    iteration(i + 1, Int<1>{});
-    if (NS > 2) iteration(i + 2, Int<2>{});
+  for (; i + 3 < nt; i += 2) {
+    iteration(i, Int<0>{}, TrueT{}, TrueT{});
+    iteration(i + 1, Int<1>{}, TrueT{}, TrueT{});
   }
-  if (i < nt - 1) iteration(i, Int<0>{});
-  if (NS > 2 && i + 1 < nt - 1) iteration(i + 1, Int<1>{});
-  // drain: the last tile's P V
-  sync_tile(nt - 1);
-  switch ((nt - 1) % NS) {
-    case 0: mfma_phase((const LDS_AS char*)vslot(Int<0>{}), nullptr, FalseT{}); break;
-    case 1: mfma_phase((const LDS_AS char*)vslot(Int<1>{}), nullptr, FalseT{}); break;
-    default: mfma_phase((const LDS_AS char*)vslot(Int<2>{}), nullptr, FalseT{}); break;
+  // i is even here and nt - i is 1, 2 or 3
+  if (i + 2 < nt) {
+    iteration(i, Int<0>{}, TrueT{}, TrueT{});
+    iteration(i + 1, Int<1>{}, FalseT{}, TrueT{});
+    iteration(i + 2, Int<0>{}, FalseT{}, FalseT{});
+  } else if (i + 1 < nt) {
+    iteration(i, Int<0>{}, FalseT{}, TrueT{});
+    iteration(i + 1, Int<1>{}, FalseT{}, FalseT{});
+  } else {
+    iteration(i, Int<0>{}, FalseT{}, FalseT{});
   }
-  if (PP && grp == 0) barrier();
 
   // ---- finalize and epilogue ------------------------------------------------
-  T* obase = (T*)a.o + head_off;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = halves_sum(l_run[qb]);
-    const float ll = halves_sum(l_lse[qb]);
-    const bool ok = lt > 0.f;  // false for 0 and NaN
-    const float inv = ok ? 1.0f / lt : 0.f;
-    const int qi = qw + qb * 32 + l32;
-    if (qi < N) {
-      if (h32 == 0) {
-        const float lse = ok ? (m_run[qb] * c + __builtin_amdgcn_logf(ll)) * kLn2 : -__builtin_inff();
-        a.lse[(int64_t)bh * N + qi] = lse;
-      }
-      T* orow = obase + (int64_t)qi * a.H * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          typedef T t4 __attribute__((ext_vector_type(4)));
-          float __attribute__((ext_vector_type(4))) f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = oacc[qb][db][4 * g + e] * inv;
-          t4 ov = __builtin_convertvector(f, t4);
-          *(u32x2*)(orow + db * 32 + 8 * g + 4 * h32) = __builtin_bit_cast(u32x2, ov);
-        }
+  const float lt = halves_sum(l_run);
+  const float ll = halves_sum(l_lse);
+  const bool ok = lt > 0.f;  // false for 0 and NaN
+  const float inv = ok ? 1.0f / lt : 0.f;
+  if (qi < N) {
+    if (h32 == 0) {
+      const float lse = ok ? (m_run * c + __builtin_amdgcn_logf(ll)) * kLn2 : -__builtin_inff();
+      a.lse[(int64_t)bh * N + qi] = lse;
     }
+    T* orow = (T*)a.o + head_off + (int64_t)qi * a.H * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        float __attribute__((ext_vector_type(4))) f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * g + e] * inv;
+        t4 ov = __builtin_convertvector(f, t4);
+        *(u32x2*)(orow + db * 32 + 8 * g + 4 * h32) = __builtin_bit_cast(u32x2, ov);
+      }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int D, int QB, int KB, bool CAUSAL, bool PP, typename T>
+template <int D, int KB, bool CAUSAL, typename T>
 int launch(const FwdArgs& f, hipStream_t st) {
-  constexpr int BM = (PP ? 256 : 128) * QB;
+  constexpr int BM = 128;
   KernelArgs a;
   a.q = f.q; a.k = f.k; a.v = f.v; a.o = f.o; a.lse = f.lse;
   a.B = f.B; a.H = f.H; a.N = f.N;
   a.n_mblk = (f.N + BM - 1) / BM;
   a.c = f.scale_log2;
   const int grid = a.n_mblk * f.B * f.H;
-  hipLaunchKernelGGL((fwd_kernel<D, QB, KB, CAUSAL, PP, T>), dim3(grid), dim3(PP ? 512 : 256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<D, KB, CAUSAL, T>), dim3(grid), dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 
-// Tile configuration per head dimension: QB = 32-row query blocks per wave,
-// KB = 32-key blocks per KV tile.
-#ifndef ATTN_D64_QB
-#define ATTN_D64_QB 1
-#endif
+// KV tile size per head dimension, in 32-key blocks.
 #ifndef ATTN_D64_KB
 #define ATTN_D64_KB 2
 #endif
-#ifndef ATTN_D128_QB
-#define ATTN_D128_QB 1
-#endif
 #ifndef ATTN_D128_KB
 #define ATTN_D128_KB 1
-#endif
-#ifndef ATTN_D64_PP
-#define ATTN_D64_PP 0
-#endif
-#ifndef ATTN_D128_PP
-#define ATTN_D128_PP 0
-#endif
-#ifndef ATTN_D256_PP
-#define ATTN_D256_PP 0
-#endif
-#ifndef ATTN_D256_QB
-#define ATTN_D256_QB 1
 #endif
 #ifndef ATTN_D256_KB
 #define ATTN_D256_KB 1
@@ -611,10 +625,8 @@ int launch(const FwdArgs& f, hipStream_t st) {
 
 template <int D, typename T>
 int dispatch_d(const FwdArgs& f, hipStream_t st) {
-  constexpr int QB = D == 64 ? ATTN_D64_QB : D == 128 ? ATTN_D128_QB : ATTN_D256_QB;
   constexpr int KB = D == 64 ? ATTN_D64_KB : D == 128 ? ATTN_D128_KB : ATTN_D256_KB;
-  constexpr bool PP = D == 64 ? ATTN_D64_PP : D == 128 ? ATTN_D128_PP : ATTN_D256_PP;
-  return f.causal ? launch<D, QB, KB, true, PP, T>(f, st) : launch<D, QB, KB, false, PP, T>(f, st);
+  return f.causal ? launch<D, KB, true, T>(f, st) : launch<D, KB, false, T>(f, st);
 }
 
 template <typename T>
