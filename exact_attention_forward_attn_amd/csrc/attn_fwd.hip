@@ -129,6 +129,7 @@ __device__ __forceinline__ int swz_v(int r) {
 #endif
 // rescale threshold of the lazy path, in base-2 exponent units
 constexpr float kTau = 8.0f;
+constexpr float kPmax = 256.0f;  // 2^kTau
 
 struct KernelArgs {
   const void* q;
@@ -164,6 +165,13 @@ struct For {
   }
 };
 
+// Waves per SIMD each kernel is compiled for (its register budget).
+#ifndef ATTN_D128_WAVES
+#define ATTN_D128_WAVES 2
+#endif
+template <int D>
+constexpr int kWavesPerEU = D == 256 ? 1 : D == 128 ? ATTN_D128_WAVES : 2;
+
 // Software pipeline of one wave (tile i = i-th KV tile in processing order):
 //
 //   block i:  S_{i+2}^T = K_{i+2} Q^T  (MFMA)
@@ -179,7 +187,7 @@ struct For {
 // LDS holds two K and two V tiles. K runs two tiles ahead of V: block i
 // reads V_i and K_{i+2} while V_{i+1} and K_{i+3} are copied in.
 template <int D, int KB, bool CAUSAL, typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>, kWavesPerEU<D>)))
 void fwd_kernel(KernelArgs a) {
   // The body is device code only; the host pass just needs the launch stub
   // (instantiating the body there makes clang drop the stub silently).
@@ -276,13 +284,17 @@ void fwd_kernel(KernelArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   const float c = a.c;
-  const float tau_c = kTau / c;
   // m_run: the exponent reference (a running max); msc = m_run * c (0 while
-  // m_run = -inf); thr = m_run + kTau / c, the largest score it covers.
-  // l_run: sum of the rounded P that entered P V (normalises O); l_lse:
-  // float32 sum of P (gives LSE).
-  float m_run = -__builtin_inff(), msc = 0.f, thr = -__builtin_inff();
-  float l_run = 0.f, l_lse = 0.f;
+  // m_run = -inf).
+  // lacc: the sum of the rounded P that entered P V, accumulated by the
+  // matrix core as ones^T P^T next to O^T (every row holds the lane's query
+  // sum; it normalises O); l_lse: float32 sum of P (gives LSE).
+  float m_run = -__builtin_inff(), msc = 0.f;
+  f32x16 lacc = {};
+  float l_lse = 0.f;
+  v8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;
@@ -300,14 +312,13 @@ void fwd_kernel(KernelArgs a) {
   auto kslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? kbuf1 : kbuf0; };
   auto vslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? vbuf1 : vbuf0; };
   // Copy tile i (in processing order) of K or V into dst. The row offset of
-  // segment t is the per-lane base plus a uniform stride; the base goes
-  // through an empty asm so the compiler cannot hoist one VGPR per
-  // (slot, segment) out of the loop.
+  // segment t is the per-lane base plus a uniform stride. (All of it goes in
+  // the VGPR offset: the buffer range check, which zero-fills rows past N,
+  // does not cover the scalar offset.)
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) ATTN_INLINE {
     const uint32_t base = (uint32_t)((nt - 1 - i) * BN) * RS;
-    uint32_t g0 = is_k ? kg[0] : vg0;
-    uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
-    asm volatile("" : "+v"(g0), "+v"(g1));
+    const uint32_t g0 = is_k ? kg[0] : vg0;
+    const uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
 #pragma unroll
     for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
       const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * 4 * G::RPS * RS);
@@ -360,52 +371,47 @@ void fwd_kernel(KernelArgs a) {
   // reference m_run moves only when some row's maximum exceeds it by more
   // than kTau base-2 units, so every p = 2^(s c - m_run c) <= 2^kTau. A tile
   // therefore nearly always keeps the current reference, and P is computed
-  // against it right away while an independent max tree checks the rule; a
-  // tile that breaks it (the first one always does) is redone after its
+  // against it right away; a tile that breaks the rule (the first one always
+  // does) is redone after its
   // block against the new reference, and O~ and l are multiplied by
   // rho = 2^((m_old - m_new) c). O = O~/l and LSE = m c + log2 l are
-  // unchanged in exact arithmetic. l_run sums the rounded p that enter P V,
-  // so O~/l_run is an exact convex combination of the weights the product
-  // used; l_lse is the float32 sum (gives the LSE).
+  // unchanged in exact arithmetic. The check needs no max: every p is at
+  // most the lane's float32 sum of its tile, so a sum <= 2^kTau proves the
+  // rule held (a reference still at -inf always takes the update, which sets
+  // it to the row maximum). O~ is normalised by the sum of the
+  // rounded p that entered P V (lacc), so O is an exact convex combination
+  // of the weights the product used; l_lse is the float32 sum (gives LSE).
   //
   // The work is cut into single VALU instructions placed on the steps of a
   // block (one MFMA each) so that no instruction waits on the one just
   // before it: score e has its fma at step f(e), its exp at f(e)+1, its
-  // float32 add and 16-bit pack at f(e)+2, the pack's dot2 at f(e)+3. Sums
-  // and maxima use two independent partials each.
+  // float32 add and 16-bit pack at f(e)+2. The sum uses two independent
+  // partials. (The sum of the rounded p is left to the
+  // matrix core: a v_dot2 next to an MFMA in flight waits for it to finish.)
   constexpr int NV = 16 * KB;  // scores per lane in a tile
   float fv[NV];
-  float pmx[2], mxv, r32p[2], r16p[2], r32v, r16v;
+  float r32p[2], r32v;
   v2 pp[NV / 2];
   bool need = false;
 
   // The step schedule of a block of M MFMA steps.
   struct Sched {
     int M;
-    constexpr int span() const { return M > 4 ? M - 3 : 1; }
+    constexpr int span() const { return M > 4 ? M - 2 : 1; }
     constexpr int f(int e) const { return (e * span()) / NV; }
-    constexpr int maxs() const { return (M / 2 < NV / 4 ? M / 2 : NV / 4) > 0 ? (M / 2 < NV / 4 ? M / 2 : NV / 4) : 1; }
-    constexpr int last() const { return f(NV - 1) + 4 > maxs() + 1 ? f(NV - 1) + 4 : maxs() + 1; }
+    constexpr int last() const { return f(NV - 1) + 3; }
   };
 
   // VALU work of step k (on the M-step schedule) for the tile in s[SB].
-  // WITH_MAX adds the max tree and the check of the reference.
-  auto sm_step = [&](auto sb_tag, auto k_tag, auto m_tag, auto max_tag) ATTN_INLINE {
+  // WITH_CHECK adds the check of the reference rule.
+  auto sm_step = [&](auto sb_tag, auto k_tag, auto m_tag, auto check_tag) ATTN_INLINE {
     constexpr int SB = decltype(sb_tag)::value;
     constexpr int K = decltype(k_tag)::value;
     constexpr Sched S{decltype(m_tag)::value};
-    constexpr bool WITH_MAX = decltype(max_tag)::value;
-    constexpr int CH = NV / S.maxs();  // scores per max step
+    constexpr bool WITH_CHECK = decltype(check_tag)::value;
     For<0, NV>::run([&](auto e_tag) ATTN_INLINE {
       constexpr int e = decltype(e_tag)::value;
       constexpr int f = S.f(e);
-      // row max: pairs of scores folded into two partials (v_max3)
-      if constexpr (WITH_MAX && e % 2 == 0 && e / CH == K) {
-        constexpr int j = ((e % CH) / 2) % 2;
-        const float x0 = s[SB][e / 16][e % 16], x1 = s[SB][(e + 1) / 16][(e + 1) % 16];
-        pmx[j] = (e < 4) ? __builtin_fmaxf(x0, x1) : __builtin_fmaxf(__builtin_fmaxf(pmx[j], x0), x1);
-        pin(pmx[j]);
-      }
       if constexpr (f == K) {
         fv[e] = __builtin_fmaf(s[SB][e / 16][e % 16], c, -msc);
         pin(fv[e]);
@@ -422,20 +428,11 @@ void fwd_kernel(KernelArgs a) {
           pin(pp[e / 2]);
         }
       }
-      if constexpr (e % 2 == 1 && f + 3 == K) {
-        constexpr int q = e / 2;
-        r16p[q % 2] = E::dot2(pp[q], q < 2 ? 0.f : r16p[q % 2]);
-        pin(r16p[q % 2]);
-      }
     });
-    if constexpr (WITH_MAX && K == S.maxs()) {
-      mxv = __builtin_fmaxf(pmx[0], pmx[1]);
-      pin(mxv);
-    }
-    if constexpr (WITH_MAX && K == S.maxs() + 1) need = __builtin_amdgcn_ballot_w64(mxv > thr) != 0;
     if constexpr (K == S.last()) {
       r32v = r32p[0] + r32p[1];
-      r16v = r16p[0] + r16p[1];
+      // !(x <= y) also catches a NaN sum
+      if constexpr (WITH_CHECK) need = __builtin_amdgcn_ballot_w64(!(r32v <= kPmax) || m_run == -__builtin_inff()) != 0;
       // the packed pairs become the B operands of the tile's P V product
 #pragma unroll
       for (int g = 0; g < 2 * KB; ++g) {
@@ -450,19 +447,20 @@ void fwd_kernel(KernelArgs a) {
   auto finish_tile = [&](auto sb_tag) ATTN_INLINE {
     constexpr int SB = decltype(sb_tag)::value;
     if (need) {
-      const float m_new = __builtin_fmaxf(m_run, halves_max(mxv));
+      float mx = s[SB][0][0];
+#pragma unroll
+      for (int e = 1; e < NV; ++e) mx = __builtin_fmaxf(mx, s[SB][e / 16][e % 16]);
+      const float m_new = __builtin_fmaxf(m_run, halves_max(mx));
       const float rho = (m_new == -__builtin_inff()) ? 1.f : exp2_fast((m_run - m_new) * c);
       m_run = m_new;
       msc = (m_new == -__builtin_inff()) ? 0.f : m_new * c;
-      thr = m_new + tau_c;
       constexpr Sched S1{1};
       For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<SB>{}, k, Int<1>{}, FalseT{}); });
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= rho;
-      l_run *= rho;
+      lacc *= rho;
       l_lse *= rho;
     }
-    l_run += r16v;
     l_lse += r32v;
   };
 
@@ -476,7 +474,7 @@ void fwd_kernel(KernelArgs a) {
     constexpr int SN = J ^ 1;
     constexpr bool DO_QK = decltype(qk_tag)::value;
     constexpr bool DO_SM = decltype(sm_tag)::value;
-    constexpr int MPV = DB * KB * 2;
+    constexpr int MPV = DB * KB * 2 + 2 * KB;  // P V, then ones^T P^T
     constexpr int MQK = DO_QK ? KC * KB : 0;
     constexpr int M = MPV + MQK;
     constexpr Sched S{M};
@@ -484,12 +482,15 @@ void fwd_kernel(KernelArgs a) {
     constexpr int LEAD = ATTN_DS_LEAD;
     const LDS_AS char* vt = (const LDS_AS char*)vslot(Int<J>{});
     const char* kt = kslot(Int<J>{});
-    // MFMA m: QK step (kc, kb) first, then PV step (db, kb, ks)
+    // MFMA m: QK step (kc, kb) first, then PV step (db, kb, ks), then the
+    // row sums (kb, ks)
     auto load_op = [&](auto m_tag) ATTN_INLINE -> v8 {
       constexpr int m = decltype(m_tag)::value;
       if constexpr (m < MQK) {
         constexpr int kc = m / KB, kb = m % KB;
         return *(const v8*)(kt + kb * 32 * G::ROWB + (kc / 8) * 256 + kofs[kc % 8]);
+      } else if constexpr (m - MQK >= DB * KB * 2) {
+        return ones;
       } else {
         constexpr int t = m - MQK;
         constexpr int db = t / (2 * KB), kb = (t / 2) % KB, ks = t % 2;
@@ -507,7 +508,12 @@ void fwd_kernel(KernelArgs a) {
       } else {
         constexpr int t = m - MQK;
         constexpr int db = t / (2 * KB), kb = (t / 2) % KB, ks = t % 2;
-        oacc[db] = E::mfma(op, pk[J][kb][ks], oacc[db]);
+        if constexpr (t < DB * KB * 2) {
+          oacc[db] = E::mfma(op, pk[J][kb][ks], oacc[db]);
+        } else {
+          constexpr int u = t - DB * KB * 2;
+          lacc = E::mfma(op, pk[J][u / 2][u % 2], lacc);
+        }
       }
     };
     v8 ring[LEAD];
@@ -574,7 +580,7 @@ void fwd_kernel(KernelArgs a) {
   }
 
   // ---- finalize and epilogue ------------------------------------------------
-  const float lt = halves_sum(l_run);
+  const float lt = lacc[0];
   const float ll = halves_sum(l_lse);
   const bool ok = lt > 0.f;  // false for 0 and NaN
   const float inv = ok ? 1.0f / lt : 0.f;
