@@ -11,6 +11,7 @@ file when --out is given.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8]
        python bench.py --copy-calibration   (plain copy kernel for PMC scaling)
+       python bench.py --gemm-ceiling       (dense bf16 GEMM reference, torch.matmul)
 """
 from __future__ import annotations
 
@@ -161,6 +162,32 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
+def gemm_ceiling():
+    """Dense bf16 GEMM (hipBLASLt via torch.matmul) on random N(0,1) and on
+    all-zero operands: the practical MFMA ceiling on this part, whose clock
+    under load depends on how much the data toggles."""
+    import torch
+    torch.manual_seed(0)
+    for (M, N, K) in [(8192, 8192, 8192), (16384, 16384, 8192)]:
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        b = torch.randn(K, N, device="cuda").to(torch.bfloat16)
+        for kind, (x, y) in (("random", (a, b)), ("zeros", (torch.zeros_like(a), torch.zeros_like(b)))):
+            for _ in range(3):
+                x @ y
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            reps = 20
+            e0.record()
+            for _ in range(reps):
+                x @ y
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            print(json.dumps({"gemm": f"{M}x{N}x{K}", "data": kind, "ms": round(ms, 4),
+                              "TFLOPS": round(2 * M * N * K / ms / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +198,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--gemm-ceiling", action="store_true", help="time dense bf16 GEMMs (torch.matmul) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -180,6 +208,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling()
         return
 
     import torch
