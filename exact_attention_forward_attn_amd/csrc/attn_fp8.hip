@@ -251,22 +251,43 @@ struct Fwd8Args {
   float c;        // alpha * log2(e)
 };
 
-#ifndef ATTN8_SB_K
-#define ATTN8_SB_K 2
-#endif
+// rescale threshold of the lazy path in base-2 units: with Max_offset 8 a
+// score at most kTau8 above the reference gives p <= 2^8.8 < 448, the e4m3
+// maximum
+constexpr float kTau8 = 0.8f;
 
-template <int D, int QB, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd8_kernel(Fwd8Args a) {
+// Waves per SIMD each kernel is compiled for (its register budget).
+template <int D>
+constexpr int kWaves8 = D == 256 ? 1 : 2;
+
+// Software pipeline of one wave, as in the 16-bit kernel (tile i = i-th KV
+// tile of 64 keys in processing order):
+//
+//   block i:  S_{i+2}^T = K_{i+2} Q^T  (MFMA, K = 64 dims per step)
+//             O^T += V_i^T P_i^T       (MFMA, K = 64 keys per step)
+//             P_{i+1} from S_{i+1}     (VALU, in the MFMA shadow)
+//
+// Descales. The score scale of tile (i, j) is ct = alpha*log2(e)*dq_i*dk_j and
+// the running max m is kept in those scaled base-2 units; P = 2^(s ct - m + 8)
+// (Max_offset 8). O~ is kept in units of the dv of the last tile added: when
+// the next tile's V block has another dv, O~ is multiplied by dv_prev/dv_cur
+// together with the rare rescale ("FlashAttention-3 on Hopper", section 6.3:
+// the descale folded into the O rescale). l sums p in float32 (the pages' row
+// sum), so O = dv_last O~ / l.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves8<D>, kWaves8<D>)))
+void fwd8_kernel(Fwd8Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef Geo8<D> G;
   constexpr int BN = G::BN;
-  constexpr int WQ = 32 * QB;
-  constexpr int BM = 4 * WQ;
+  constexpr int BM = 128;
   constexpr int KC = D / 64;     // k-steps of QK^T (64 dims each)
   constexpr int DB = D / 32;
-  static_assert(WQ <= 128 && 128 % WQ == 0, "a wave's rows must sit in one 128-row scale block");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * G::STAGE];
+  __shared__ __attribute__((aligned(1024))) char kbuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[G::TILE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -280,7 +301,8 @@ __global__ __launch_bounds__(256) void fwd8_kernel(Fwd8Args a) {
   const int hh = bh % a.H;
   const int N = a.N;
   const int q0 = mblk * BM;
-  const int qw = q0 + wave * WQ;
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
   const uint32_t RS = (uint32_t)a.H * D;
   const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;
   const uint32_t span = (uint32_t)(N - 1) * RS + D;
@@ -289,28 +311,25 @@ __global__ __launch_bounds__(256) void fwd8_kernel(Fwd8Args a) {
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + head_off, span);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + head_off, span);
 
-  // descales of this head: index j of the 128-row block, or 0 per tensor
-  const float* dqh = a.dq + (a.nsb ? (int64_t)bh * a.nsb : 0);
-  const float* dkh = a.dk + (a.nsb ? (int64_t)bh * a.nsb : 0);
-  const float* dvh = a.dv + (a.nsb ? (int64_t)bh * a.nsb : 0);
-  auto sblk = [&](int row) { return a.nsb ? row / 128 : 0; };
+  // descales of this head: one per 128-row block, or one per tensor
+  const int nsb = a.nsb;
+  const int64_t sb0 = nsb ? (int64_t)bh * nsb : 0;
+  const uint32_t nsb_bytes = (uint32_t)(nsb ? nsb : 1) * 4;
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + sb0, nsb_bytes);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + sb0, nsb_bytes);
+  auto sblk = [&](int row) ATTN_INLINE { return nsb ? row / 128 : 0; };
 
-  // Q^T operands: dims 64kc + 32*h32 .. +31 of query row qw + 32qb + l32
-  i32x8 qreg[QB][KC];
-  float cq[QB];
+  // Q^T operands: dims 64kc + 32*h32 .. +31 of query row qi
+  i32x8 qreg[KC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const uint32_t row = (uint32_t)(qw + qb * 32 + l32);
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const uint32_t off = row * RS + 64 * kc + 32 * h32;
-      u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-      u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
-      qreg[qb][kc] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    const int qrow = min(qw + qb * 32, N - 1);
-    cq[qb] = a.c * dqh[sblk(qrow)];
+  for (int kc = 0; kc < KC; ++kc) {
+    const uint32_t off = (uint32_t)qi * RS + 64 * kc + 32 * h32;
+    u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+    u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+    qreg[kc] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
+  // the wave's 32 rows sit in one 128-row scale block
+  const float cq = a.c * a.dq[sb0 + sblk(min(qw, N - 1))];
 
   uint32_t kg[G::SEG_PER_WAVE], vg[G::SEG_PER_WAVE];
 #pragma unroll
@@ -339,191 +358,303 @@ __global__ __launch_bounds__(256) void fwd8_kernel(Fwd8Args a) {
     for (int db = 0; db < DB; ++db) vofs[db] = r0 * G::ROWB + (((2 * db + dh) ^ sw) << 4) + 8 * (p & 1);
   }
 
-  f32x16 oacc[QB][DB];
-  float m_run[QB], l_run[QB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -__builtin_inff();
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16{};
-  }
-  float dv_prev = 1.f;
-  bool first = true;
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  // m_run: the reference (scaled base-2 units); l_run: float32 sum of p;
+  // dv_cur: the dv whose units O~ is in
+  float m_run = -__builtin_inff(), l_run = 0.f, dv_cur = 1.f;
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;
+  // masked tiles form a prefix of the descending order (as in the 16-bit kernel)
+  int jm = N >= BN ? (N - BN) / BN + 1 : 0;
+  if (CAUSAL) {
+    const int x = qw - BN + 1;
+    jm = min(jm, x >= 0 ? x / BN + 1 : 0);
+  }
+  const int n_masked = max(0, nt - jm);
 
-  auto issue_tile = [&](int kv0, int st) {
-    const uint32_t base = (uint32_t)kv0 * RS;
+  auto kslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? kbuf1 : kbuf0; };
+  auto vslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? vbuf1 : vbuf0; };
+  auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) ATTN_INLINE {
+    const uint32_t base = (uint32_t)((nt - 1 - i) * BN) * RS;
 #pragma unroll
     for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
-      const int seg = wave + 4 * t;
-      char* kdst = smem + st * G::STAGE + seg * 1024;
-      char* vdst = smem + st * G::STAGE + G::TILE + seg * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (LDS_AS void*)kdst, 16, base + kg[t], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (LDS_AS void*)vdst, 16, base + vg[t], 0, 0, 0);
+      const uint32_t voff = (is_k ? kg[t] : vg[t]) + base;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + 4 * t) * 1024), 16, voff, 0, 0, 0);
     }
   };
+  auto barrier = [&]() ATTN_INLINE {
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  auto process = [&](const char* kt, const LDS_AS char* vt, int kv0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 s[2][QB];
+  f32x16 s[2][2];    // S^T of two tiles (tile parity) x two 32-key blocks
+  i32x8 p8[2];       // P of two tiles as e4m3 bytes (the K = 64 B operand)
+  float dkt[2], dvt[2];  // descales of two tiles (tile parity)
+  // descales of tile i into slot X (vector loads: they complete with the
+  // tile copies, under the same vmcnt wait)
+  auto load_desc = [&](auto x_tag, int i) ATTN_INLINE {
+    constexpr int X = decltype(x_tag)::value & 1;
+    const uint32_t off = (uint32_t)sblk((nt - 1 - i) * BN) * 4;
+    dkt[X] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdk, off, 0, 0));
+    dvt[X] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdv, off, 0, 0));
+  };
+
+  auto qk = [&](auto sb_tag, const char* kt) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
+#pragma unroll
+    for (int t = 0; t < KC * 2; ++t) {
+      const int kc = t / 2, kb = t % 2;
+      const u32x4 lo = *(const u32x4*)(kt + kb * 32 * G::ROWB + kofs[kc][0]);
+      const u32x4 hi = *(const u32x4*)(kt + kb * 32 * G::ROWB + kofs[kc][1]);
+      const i32x8 ka = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      s[SB][kb] = mfma8(ka, qreg[kc], kc == 0 ? f32x16{} : s[SB][kb]);
+    }
+  };
+  auto apply_mask = [&](auto sb_tag, int kv0) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
+    const int tn = N - kv0 - 4 * h32;
+    const int tc = qi - kv0 - 4 * h32;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      if (kc % ATTN8_SB_K == 0) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 lo = *(const u32x4*)(kt + kb * 32 * G::ROWB + kofs[kc][0]);
-        const u32x4 hi = *(const u32x4*)(kt + kb * 32 * G::ROWB + kofs[kc][1]);
-        const i32x8 ka = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma8(ka, qreg[qb][kc], s[kb][qb]);
+      for (int r = 0; r < 16; ++r) {
+        const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
+        if (o >= tn || (CAUSAL && o > tc)) s[SB][kb][r] = -__builtin_inff();
       }
-    }
-    if (MASKED) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qi = qw + qb * 32 + l32;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-            if (key >= N || (CAUSAL && key > qi)) s[kb][qb][r] = -__builtin_inff();
-          }
-      }
-    }
-    const float dk_t = dkh[sblk(kv0)];
-    const float dv_t = dvh[sblk(kv0)];
-    const float dv_ratio = first ? 1.f : dv_prev / dv_t;
-    i32x8 p8[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float ct = cq[qb] * dk_t;
-      float mx = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][qb][r]);
-      mx = halves_max(mx) * ct;
-      const float m_new = __builtin_fmaxf(m_run[qb], mx);
-      const float ref = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float rho = exp2_fast(m_run[qb] - ref);
-      m_run[qb] = m_new;
-      const float off = 8.0f - ref;  // Max_offset: the row maximum maps to 2^8
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(__builtin_fmaf(s[kb][qb][r], ct, off));
-          s[kb][qb][r] = p;
-          rs += p;
-        }
-      l_run[qb] = l_run[qb] * rho + rs;
-      const float f = rho * dv_ratio;
-      if (__builtin_amdgcn_ballot_w64(f != 1.0f) != 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[qb][db] *= f;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          p8[qb][4 * kb + g] = (int)pack_e4m3(s[kb][qb][4 * g], s[kb][qb][4 * g + 1], s[kb][qb][4 * g + 2],
-                                              s[kb][qb][4 * g + 3]);
-    }
-    dv_prev = dv_t;
-    first = false;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      if (db % 2 == 0) __builtin_amdgcn_sched_barrier(0);
-      i32x8 va;
-#pragma unroll
-      for (int rd = 0; rd < 4; ++rd) {
-        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(vt + vofs[db] + 16 * rd * G::ROWB));
-        va[2 * rd] = w[0];
-        va[2 * rd + 1] = w[1];
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma8(va, p8[qb], oacc[qb][db]);
-    }
   };
 
-  if (nt > 0) issue_tile((nt - 1) * BN, 0);
-  for (int it = 0; it < nt; ++it) {
-    const int kv0 = (nt - 1 - it) * BN;
-    const int st = it & 1;
-    if (it + 1 < nt) {
-      issue_tile(kv0 - BN, st ^ 1);
-      wait_vmcnt<2 * G::SEG_PER_WAVE>();
-    } else {
-      wait_vmcnt<0>();
+  // ---- online softmax of one tile (32 scores per lane) -----------------------
+  // Conditional rescale ("FlashAttention v1-v4", FA4 section) with threshold
+  // kTau8: p is computed against the current reference while a max tree
+  // checks the rule; a tile that breaks it (always the first) is redone after
+  // its block, and O~ and l are multiplied by rho = 2^(m_old - m_new).
+  constexpr int NV = 32;
+  float fv[NV];
+  float pmx[2], mxv, r32p[2], r32v;
+  float ct, ot;  // per-tile score scale and exponent offset
+  uint32_t pw[8];
+  bool need = false;
+
+  struct Sched {
+    int M;
+    constexpr int span() const { return M > 3 ? M - 2 : 1; }
+    constexpr int f(int e) const { return (e * span()) / NV; }
+    constexpr int maxs() const { return M / 2 > 0 ? M / 2 : 1; }
+    constexpr int last() const { return f(NV - 1) + 3 > maxs() + 1 ? f(NV - 1) + 3 : maxs() + 1; }
+  };
+
+  // per-tile scalars for the tile with descale slot X
+  auto tile_scalars = [&](auto x_tag) ATTN_INLINE {
+    constexpr int X = decltype(x_tag)::value & 1;
+    ct = cq * dkt[X];
+    // exponent offset: Max_offset 8 minus the reference
+    ot = (m_run == -__builtin_inff() ? 0.f : -m_run) + 8.0f;
+  };
+
+  auto sm_step = [&](auto sb_tag, auto k_tag, auto m_tag, auto max_tag) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
+    constexpr int K = decltype(k_tag)::value;
+    constexpr Sched S{decltype(m_tag)::value};
+    constexpr bool WITH_MAX = decltype(max_tag)::value;
+    constexpr int CH = NV / S.maxs();  // scores per max step
+    For<0, NV>::run([&](auto e_tag) ATTN_INLINE {
+      constexpr int e = decltype(e_tag)::value;
+      constexpr int f = S.f(e);
+      if constexpr (WITH_MAX && e % 2 == 0 && e / CH == K) {
+        constexpr int j = ((e % CH) / 2) % 2;
+        const float x0 = s[SB][e / 16][e % 16], x1 = s[SB][(e + 1) / 16][(e + 1) % 16];
+        pmx[j] = (e < 4) ? __builtin_fmaxf(x0, x1) : __builtin_fmaxf(__builtin_fmaxf(pmx[j], x0), x1);
+        pin(pmx[j]);
+      }
+      if constexpr (f == K) {
+        fv[e] = __builtin_fmaf(s[SB][e / 16][e % 16], ct, ot);
+        pin(fv[e]);
+      }
+      if constexpr (f + 1 == K) {
+        fv[e] = exp2_fast(fv[e]);
+        pin(fv[e]);
+      }
+      if constexpr (f + 2 == K) {
+        r32p[e % 2] = e < 2 ? fv[e] : r32p[e % 2] + fv[e];
+        pin(r32p[e % 2]);
+        if constexpr (e % 4 == 3) {
+          pw[e / 4] = pack_e4m3(fv[e - 3], fv[e - 2], fv[e - 1], fv[e]);
+          pin(pw[e / 4]);
+        }
+      }
+    });
+    if constexpr (WITH_MAX && K == S.maxs()) {
+      mxv = __builtin_fmaxf(pmx[0], pmx[1]);
+      pin(mxv);
     }
-    __builtin_amdgcn_s_barrier();
-    const bool skip = (CAUSAL && kv0 > qw + WQ - 1) || qw >= N;
-    if (!skip) {
-      const char* kt = smem + st * G::STAGE;
-      const LDS_AS char* vt = (const LDS_AS char*)(smem + st * G::STAGE + G::TILE);
-      const bool masked = (kv0 + BN > N) || (CAUSAL && kv0 + BN - 1 > qw);
-      if (masked)
-        process(kt, vt, kv0, TrueT{});
-      else
-        process(kt, vt, kv0, FalseT{});
+    if constexpr (WITH_MAX && K == S.maxs() + 1)
+      need = __builtin_amdgcn_ballot_w64(mxv * ct > m_run + kTau8 || m_run == -__builtin_inff()) != 0;
+    if constexpr (K == S.last()) {
+      r32v = r32p[0] + r32p[1];
+      i32x8 w;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) w[g] = (int)pw[g];
+      p8[SB] = w;
     }
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_barrier();
+  };
+  // After the block that added tile j-1 to O~: the rare reference update for
+  // tile j, and O~ moved to tile j's dv units.
+  auto finish_tile = [&](auto sb_tag) ATTN_INLINE {
+    constexpr int SB = decltype(sb_tag)::value;
+    float f = 1.f;
+    if (need) {
+      const float mt = halves_max(mxv) * ct;
+      const float m_new = __builtin_fmaxf(m_run, mt);
+      f = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      ot = (m_new == -__builtin_inff() ? 0.f : -m_new) + 8.0f;
+      constexpr Sched S1{1};
+      For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<SB>{}, k, Int<1>{}, FalseT{}); });
+      l_run *= f;
+    }
+    const float dvr = dv_cur / dvt[SB];
+    dv_cur = dvt[SB];
+    if (need || dvr != 1.f) {
+      f *= dvr;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= f;
+    }
+    l_run += r32v;
+  };
+
+  auto block = [&](auto j_tag, auto qk_tag, auto sm_tag) ATTN_INLINE {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr int SN = J ^ 1;
+    constexpr bool DO_QK = decltype(qk_tag)::value;
+    constexpr bool DO_SM = decltype(sm_tag)::value;
+    constexpr int MQK = DO_QK ? KC * 2 : 0;
+    constexpr int M = MQK + DB;
+    constexpr Sched S{M};
+    constexpr int STEPS = DO_SM ? (S.last() + 1 > M ? S.last() + 1 : M) : M;
+    const LDS_AS char* vt = (const LDS_AS char*)vslot(Int<J>{});
+    const char* kt = kslot(Int<J>{});
+    auto load_op = [&](auto m_tag) ATTN_INLINE -> i32x8 {
+      constexpr int m = decltype(m_tag)::value;
+      if constexpr (m < MQK) {
+        constexpr int kc = m / 2, kb = m % 2;
+        const u32x4 lo = *(const u32x4*)(kt + kb * 32 * G::ROWB + kofs[kc][0]);
+        const u32x4 hi = *(const u32x4*)(kt + kb * 32 * G::ROWB + kofs[kc][1]);
+        return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        constexpr int db = m - MQK;
+        i32x8 va;
+#pragma unroll
+        for (int rd = 0; rd < 4; ++rd) {
+          const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2*)(vt + vofs[db] + 16 * rd * G::ROWB));
+          va[2 * rd] = w[0];
+          va[2 * rd + 1] = w[1];
+        }
+        return va;
+      }
+    };
+    auto mfma_op = [&](auto m_tag, i32x8 op) ATTN_INLINE {
+      constexpr int m = decltype(m_tag)::value;
+      if constexpr (m < MQK) {
+        constexpr int kc = m / 2, kb = m % 2;
+        s[J][kb] = mfma8(op, qreg[kc], kc == 0 ? f32x16{} : s[J][kb]);
+      } else {
+        oacc[m - MQK] = mfma8(op, p8[J], oacc[m - MQK]);
+      }
+    };
+    if constexpr (DO_SM) tile_scalars(Int<SN>{});
+    i32x8 ring[2];
+    For<0, (2 < M ? 2 : M)>::run([&](auto m) ATTN_INLINE { ring[decltype(m)::value % 2] = load_op(m); });
+    For<0, STEPS>::run([&](auto k_tag) ATTN_INLINE {
+      constexpr int k = decltype(k_tag)::value;
+      if constexpr (k < M) {
+        mfma_op(k_tag, ring[k % 2]);
+        if constexpr (k + 2 < M) ring[k % 2] = load_op(Int<k + 2>{});
+      }
+      if constexpr (DO_SM) sm_step(Int<SN>{}, k_tag, Int<M>{}, TrueT{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (DO_SM) finish_tile(Int<SN>{});
+  };
+
+  // prologue: K_0, K_1, V_0 and the descales of tiles 0, 1; S_0, S_1; P_0
+  issue(rk, true, kbuf0, 0);
+  if (nt > 1) issue(rk, true, kbuf1, 1);
+  issue(rv, false, vbuf0, 0);
+  load_desc(Int<0>{}, 0);
+  if (nt > 1) load_desc(Int<1>{}, 1);
+  wait_vmcnt<0>();
+  barrier();
+  qk(Int<0>{}, kbuf0);
+  if (nt > 1) qk(Int<1>{}, kbuf1);
+  barrier();
+  if (nt > 2) issue(rk, true, kbuf0, 2);
+  if (n_masked > 0) apply_mask(Int<0>{}, (nt - 1) * BN);
+  if (n_masked > 1) apply_mask(Int<1>{}, (nt - 2) * BN);
+  {
+    tile_scalars(Int<0>{});
+    constexpr Sched S0{8};
+    For<0, S0.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<8>{}, TrueT{}); });
+    finish_tile(Int<0>{});
   }
 
-  // finalize: O = O~ * dv_last / l, LSE = (m + log2 l - 8) ln 2
-  __bf16* obase = a.o + head_off;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = halves_sum(l_run[qb]);
-    const bool ok = lt > 0.f;
-    const float inv = ok ? dv_prev / lt : 0.f;
-    const int qi = qw + qb * 32 + l32;
-    if (qi < N) {
-      if (h32 == 0) {
-        const float lse = ok ? (m_run[qb] + __builtin_amdgcn_logf(lt) - 8.0f) * kLn2 : -__builtin_inff();
-        a.lse[(int64_t)bh * N + qi] = lse;
-      }
-      __bf16* orow = obase + (int64_t)qi * a.H * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = oacc[qb][db][4 * g + e] * inv;
-          bf16x4 ov = __builtin_convertvector(f, bf16x4);
-          *(u32x2*)(orow + db * 32 + 8 * g + 4 * h32) = __builtin_bit_cast(u32x2, ov);
-        }
+  auto iteration = [&](int i, auto j_tag, auto qk_tag, auto sm_tag) ATTN_INLINE {
+    constexpr int J = decltype(j_tag)::value;
+    wait_vmcnt<0>();
+    barrier();
+    if (i + 1 < nt) issue(rv, false, vslot(Int<J + 1>{}), i + 1);
+    if (i + 3 < nt) issue(rk, true, kslot(Int<J + 1>{}), i + 3);
+    if (i + 2 < nt) load_desc(Int<J>{}, i + 2);
+    block(j_tag, qk_tag, sm_tag);
+    if (decltype(qk_tag)::value && i + 2 < n_masked) apply_mask(Int<J>{}, (nt - 3 - i) * BN);
+  };
+  int i = 0;
+  for (; i + 3 < nt; i += 2) {
+    iteration(i, Int<0>{}, TrueT{}, TrueT{});
+    iteration(i + 1, Int<1>{}, TrueT{}, TrueT{});
+  }
+  if (i + 2 < nt) {
+    iteration(i, Int<0>{}, TrueT{}, TrueT{});
+    iteration(i + 1, Int<1>{}, FalseT{}, TrueT{});
+    iteration(i + 2, Int<0>{}, FalseT{}, FalseT{});
+  } else if (i + 1 < nt) {
+    iteration(i, Int<0>{}, FalseT{}, TrueT{});
+    iteration(i + 1, Int<1>{}, FalseT{}, FalseT{});
+  } else {
+    iteration(i, Int<0>{}, FalseT{}, FalseT{});
+  }
+
+  // finalize: O = O~ dv_cur / l, LSE = (m + log2 l - 8) ln 2
+  const float lt = halves_sum(l_run);
+  const bool ok = lt > 0.f;
+  const float inv = ok ? dv_cur / lt : 0.f;
+  if (qi < N) {
+    if (h32 == 0) {
+      const float lse = ok ? (m_run + __builtin_amdgcn_logf(lt) - 8.0f) * kLn2 : -__builtin_inff();
+      a.lse[(int64_t)bh * N + qi] = lse;
     }
+    __bf16* orow = a.o + head_off + (int64_t)qi * a.H * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * g + e] * inv;
+        bf16x4 ov = __builtin_convertvector(f, bf16x4);
+        *(u32x2*)(orow + db * 32 + 8 * g + 4 * h32) = __builtin_bit_cast(u32x2, ov);
+      }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-#ifndef ATTN8_D64_QB
-#define ATTN8_D64_QB 2
-#endif
-#ifndef ATTN8_D128_QB
-#define ATTN8_D128_QB 1
-#endif
-#ifndef ATTN8_D256_QB
-#define ATTN8_D256_QB 1
-#endif
-
 template <int D, bool CAUSAL>
 int launch_fwd(const FwdArgs& f, hipStream_t st) {
-  constexpr int QB = D == 64 ? ATTN8_D64_QB : D == 128 ? ATTN8_D128_QB : ATTN8_D256_QB;
-  constexpr int BM = 128 * QB;
+  constexpr int BM = 128;
   Fwd8Args a;
   a.q = (const uint8_t*)f.q; a.k = (const uint8_t*)f.k; a.v = (const uint8_t*)f.v;
   a.o = (__bf16*)f.o; a.lse = f.lse;
@@ -533,7 +664,7 @@ int launch_fwd(const FwdArgs& f, hipStream_t st) {
   a.nsb = f.block_rows ? (f.N + f.block_rows - 1) / f.block_rows : 0;
   a.c = f.scale_log2;
   const int grid = a.n_mblk * f.B * f.H;
-  hipLaunchKernelGGL((fwd8_kernel<D, QB, CAUSAL>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(grid), dim3(256), 0, st, a);
   return (int)hipGetLastError();
 }
 

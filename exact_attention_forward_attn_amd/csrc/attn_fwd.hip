@@ -142,29 +142,6 @@ struct KernelArgs {
   float c;        // alpha * log2(e)
 };
 
-// Lambdas of the kernels are always inlined (their captures must stay in
-// registers).
-#define ATTN_INLINE __attribute__((always_inline))
-
-// Empty asm that takes x in VGPRs and may change it: the computation of x
-// cannot move past this point, which keeps work inside its pipeline step.
-template <typename X>
-__device__ __forceinline__ void pin(X& x) {
-  asm volatile("" : "+v"(x));
-}
-
-// Compile-time loop: f(Int<u>) for u = B .. E-1.
-template <int B, int E>
-struct For {
-  template <typename F>
-  static __device__ __forceinline__ void run(F&& f) {
-    if constexpr (B < E) {
-      f(Int<B>{});
-      For<B + 1, E>::run(f);
-    }
-  }
-};
-
 // Waves per SIMD each kernel is compiled for (its register budget).
 #ifndef ATTN_D128_WAVES
 #define ATTN_D128_WAVES 2

@@ -123,5 +123,28 @@ __device__ __forceinline__ int swz_rows(int r) {
   return ROWB >= 256 ? (r & 15) : ROWB == 128 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
 }
 
+// Lambdas of the kernels are always inlined (their captures must stay in
+// registers).
+#define ATTN_INLINE __attribute__((always_inline))
+
+// Empty asm that takes x in VGPRs and may change it: the computation of x
+// cannot move past this point, which keeps work inside its pipeline step.
+template <typename X>
+__device__ __forceinline__ void pin(X& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Compile-time loop: f(Int<u>) for u = B .. E-1.
+template <int B, int E>
+struct For {
+  template <typename F>
+  static __device__ __forceinline__ void run(F&& f) {
+    if constexpr (B < E) {
+      f(Int<B>{});
+      For<B + 1, E>::run(f);
+    }
+  }
+};
+
 }  // namespace dev
 }  // namespace attn
