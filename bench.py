@@ -27,11 +27,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}  # MI355X dense MFMA
-PEAK_HBM_GBS = 8000.0
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 METRIC = "attention fwd TFLOPS + % of MFMA peak, bf16 d=128 N=8k (and fp8)"
 HEADLINE = dict(B=2, N=8192, H=16, d=128, causal=False)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_d128_n8192.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_forward_attn_amd", "csrc", "attn_fwd.hip")
+
+
+def compulsory_bytes(B, N, H, d):
+    """Q, K, V read and O written once (16-bit), plus the fp32 LSE."""
+    return 8.0 * B * N * H * d + 4.0 * B * H * N
 
 
 def flops(B, N, H, d, causal):
@@ -57,8 +62,11 @@ def device_inputs(B, N, H, d, seed=0, outliers=None):
     return [torch.from_numpy(t).cuda().to(torch.bfloat16) for t in (q, k, v)]
 
 
-def time_launches(fn, steps, warmup):
-    """Runs fn warmup + steps times; returns (total_ms, per-launch ms list)."""
+def time_launches(fn, steps, warmup, flush=None):
+    """Runs fn warmup + steps times; returns (total_ms, per-launch ms list).
+    flush, when given, runs before each timed launch outside its events (it
+    evicts the inputs from the on-package cache for the short, HBM-bound
+    configurations)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -70,12 +78,26 @@ def time_launches(fn, steps, warmup):
     torch.cuda.synchronize()
     t0.record(stream)
     for a, b in ev:
+        if flush is not None:
+            flush()
         a.record(stream)
         fn()
         b.record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+
+
+_FLUSH_BUF = None
+
+
+def mall_flush():
+    """Writes 512 MiB (twice the 256 MB MALL) so the next launch reads HBM."""
+    global _FLUSH_BUF
+    import torch
+    if _FLUSH_BUF is None:
+        _FLUSH_BUF = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    _FLUSH_BUF.fill_(1)
 
 
 def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
@@ -87,9 +109,19 @@ def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
     total, per = time_launches(fn, steps, warmup)
     per_ms = sum(per) / len(per)
     tf = flops(B, N, H, d, causal) / (per_ms * 1e-3) / 1e12
-    return {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "ms_total": total,
-            "TFLOPS": tf, "frac_peak": tf / PEAK_TFLOPS["bf16"],
-            "hbm_GBs": 8.0 * B * N * H * d / (per_ms * 1e-3) / 1e9}
+    r = {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "ms_total": total,
+         "TFLOPS": tf, "frac_peak": tf / PEAK_TFLOPS["bf16"],
+         "hbm_GBs": compulsory_bytes(B, N, H, d) / (per_ms * 1e-3) / 1e9}
+    if causal:
+        r["TFLOPS_exact_causal_count"] = tf * (1 + 1 / N)
+    if N <= 1024:
+        # HBM-bound range: also time with the inputs evicted from the MALL
+        _, perc = time_launches(fn, steps, 1, flush=mall_flush)
+        msc = sum(perc) / len(perc)
+        r["ms_cold"] = msc
+        r["hbm_GBs_cold"] = compulsory_bytes(B, N, H, d) / (msc * 1e-3) / 1e9
+        r["hbm_frac_cold"] = r["hbm_GBs_cold"] / PEAK_HBM_GBS
+    return r
 
 
 def bench_fp8(ea, B, N, H, d, causal, steps, warmup):
