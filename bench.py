@@ -194,6 +194,30 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
+def gemm_tflops(M, N, K, zeros=False, reps=20):
+    """Dense bf16 GEMM throughput (hipBLASLt via torch.matmul) on N(0,1) (or
+    all-zero) operands."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+    if zeros:
+        a.zero_()
+        b.zero_()
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return 2 * M * N * K / ms / 1e9
+
+
 def gemm_ceiling():
     """Dense bf16 GEMM (hipBLASLt via torch.matmul) on random N(0,1) and on
     all-zero operands: the practical MFMA ceiling on this part, whose clock
@@ -282,6 +306,10 @@ def main():
             log("fp8 unavailable:", e)
             fp8_res = None
 
+    # the practical dense bf16 ceiling on this machine, same kind of data
+    gemm = gemm_tflops(16384, 16384, 8192)
+    log("gemm_ceiling", json.dumps({"gemm": "16384x16384x8192 bf16, N(0,1)", "TFLOPS": gemm}))
+
     cpu = None if args.no_cpu else cpu_baseline()
     if cpu:
         log("cpu_baseline", json.dumps(cpu))
@@ -307,7 +335,11 @@ def main():
                    "causal": h["causal"], "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": traffic_entry()},
+                     "traffic": traffic_entry(),
+                     "practical_ceiling": {"what": "hipBLASLt dense bf16 GEMM 16384x16384x8192 on N(0,1) "
+                                                    "data, same run (the part is power-limited below its "
+                                                    "nominal clock)",
+                                           "TFLOPS": round(gemm, 1), "frac": round(achieved / gemm, 4)}},
         "cpu_baseline": cpu,
     }
     if fp8_res:
