@@ -14,12 +14,14 @@ Contents
 --------
 attention   plain definition O = softmax(alpha Q K^T) V with LSE, the online
             (m, l, O~) recurrence, the block-combine rule, sampled rows.
+attention_bwd  gradients dQ, dK, dV of the plain definition.
 fp8         Sylvester Hadamard matrix, fast Walsh-Hadamard transform, the
             splitmix64 sign generator, OCP e4m3 encode/decode, block
             quantisation, and the fp8-emulating reference.
 
 Every function names the passage of the pages it follows. Pins (tests that
 check the oracle against something other than itself) live in
-``tests/test_oracle.py`` and ``tests/test_oracle_fp8.py``.
+``tests/test_oracle.py``, ``tests/test_oracle_bwd.py`` and
+``tests/test_oracle_fp8.py``.
 """
-from . import attention, fp8  # noqa: F401
+from . import attention, attention_bwd, fp8  # noqa: F401

@@ -1,0 +1,75 @@
+"""Attention backward, plain float64 definition (test infrastructure only).
+
+Sources: "FlashAttention-3 on Hopper", chapter 7 ("The FA3 Backward Pass:
+Algorithm"):
+
+* section 7.1: with S = alpha Q K^T, P = softmax(S) row-wise and O = P V, an
+  upstream gradient dO gives dV = P^T dO, dP = dO V^T, dS = P o (dP - D) with
+  D_i = <P_i, dP_i> (the contracted softmax Jacobian, section 7.1.1),
+  dQ = alpha dS K and dK = alpha dS^T Q (product rule on the two GEMMs);
+* section 7.1.2: D_i = rowsum(dO_i o O_i), equal to <P_i, dP_i> because
+  dP = dO V^T and O = P V;
+* masked scores are -inf in S, so their P and dS are 0 and they contribute to
+  no gradient (section 3.1 of the same page for the mask convention).
+
+The functions materialise S and P for one (b, h) and a chunk of query rows at
+a time. Layouts as in ``oracle.attention``: q, k, v, do are (B, N, H, d);
+the gradients are returned as (B, N, H, d) float64.
+
+The GPU backward shares no code with this module.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import causal_mask
+
+__all__ = ["attention_backward", "attention_backward_head"]
+
+
+def attention_backward_head(q, k, v, do, alpha, causal=False, row_chunk=1024):
+    """Gradients (dq, dk, dv) of one head: q, k, v, do are (N, d) float64."""
+    n = q.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, n, row_chunk):
+        r1 = min(n, r0 + row_chunk)
+        s = alpha * (q[r0:r1] @ k.T)
+        if causal:
+            s = np.where(causal_mask(n, n)[r0:r1], -np.inf, s)
+        m = s.max(axis=1, keepdims=True)
+        live = np.isfinite(m)
+        e = np.where(live, np.exp(s - np.where(live, m, 0.0)), 0.0)
+        den = e.sum(axis=1, keepdims=True)
+        p = np.where(den > 0, e / np.where(den > 0, den, 1.0), 0.0)
+        o = p @ v
+        dv += p.T @ do[r0:r1]
+        dp = do[r0:r1] @ v.T
+        d_i = np.sum(do[r0:r1] * o, axis=1, keepdims=True)
+        ds = p * (dp - d_i)
+        dq[r0:r1] = alpha * (ds @ k)
+        dk += alpha * (ds.T @ q[r0:r1])
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, alpha=None, causal=False, row_chunk=1024):
+    """Gradients of sum(O o dO) with respect to q, k, v (all (B, N, H, d))."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, N, H, d = q.shape
+    if alpha is None:
+        alpha = 1.0 / np.sqrt(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            gq, gk, gv = attention_backward_head(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :],
+                                                 alpha, causal, row_chunk)
+            dq[b, :, h, :] = gq
+            dk[b, :, h, :] = gk
+            dv[b, :, h, :] = gv
+    return dq, dk, dv

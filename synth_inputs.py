@@ -12,6 +12,9 @@ Hopper", section 6.4):
 * ``rng = numpy.random.default_rng(seed)``; draw Q, then K, then V, each as
   ``rng.standard_normal((B, N, H, d), dtype=float32)`` (layout B, N, H, d).
 * Round to bfloat16 (or float16) with round-to-nearest-even.
+* The upstream gradient dO of the backward is drawn from its own generator,
+  ``default_rng([seed, 1])``, as one ``standard_normal((B, N, H, d), float32)``
+  draw rounded the same way, so it does not disturb the Q, K, V stream.
 * Outliers (optional): an i.i.d. Bernoulli(rate) mask per element, independent
   for Q, K and V, drawn from the same generator after the base draws.
   ``kind="scale"`` multiplies the selected entries by ``factor`` (10);
@@ -29,6 +32,7 @@ __all__ = [
     "f16_bits_to_f32",
     "make_qkv",
     "make_qkv_f32",
+    "make_dout",
 ]
 
 
@@ -111,3 +115,16 @@ def make_qkv(B, N, H, d, seed=0, dtype="bf16", outliers=None):
     bits = tuple(enc(t) for t in (q, k, v))
     vals = tuple(dec(b).astype(np.float64) for b in bits)
     return bits, vals
+
+
+def make_dout(B, N, H, d, seed=0, dtype="bf16"):
+    """Seeded upstream gradient dO, rounded like ``make_qkv``: (bits, values)."""
+    rng = np.random.default_rng([seed, 1])
+    g = rng.standard_normal((B, N, H, d), dtype=np.float32)
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(g)
+        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+    if dtype == "f16":
+        bits = f32_to_f16_bits(g)
+        return bits, f16_bits_to_f32(bits).astype(np.float64)
+    raise ValueError(dtype)

@@ -1,0 +1,106 @@
+"""Pins for the backward oracle (CPU only).
+
+Each check is independent of the formulas the oracle is written with (section
+7.1 of "FlashAttention-3 on Hopper"): central finite differences of the
+forward oracle, torch float64 autograd through a plain torch forward (its own
+softmax derivative), and invariants of the attention function itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import attention
+from oracle.attention_bwd import attention_backward
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _loss(q, k, v, do, alpha, causal):
+    o, _ = attention(q, k, v, alpha, causal)
+    return float(np.sum(o * do))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_central_differences(causal):
+    B, N, H, d = 1, 5, 2, 3
+    q, k, v, do = (_rand((B, N, H, d), s) for s in range(4))
+    alpha = 0.7
+    dq, dk, dv = attention_backward(q, k, v, do, alpha, causal)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, alpha, causal)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, alpha, causal)
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd(causal):
+    B, N, H, d = 2, 37, 2, 16
+    q, k, v, do = (_rand((B, N, H, d), 10 + s) for s in range(4))
+    alpha = 1.0 / np.sqrt(d)
+    dq, dk, dv = attention_backward(q, k, v, do, alpha, causal)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    # plain torch forward in (B, H, N, d) with torch's own softmax
+    qh, kh, vh = (t.permute(0, 2, 1, 3) for t in (tq, tk, tv))
+    s = alpha * torch.matmul(qh, kh.transpose(-1, -2).contiguous())
+    if causal:
+        mask = torch.triu(torch.ones(N, N, dtype=torch.bool), diagonal=1)
+        s = s.masked_fill(mask, float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), vh).permute(0, 2, 1, 3)
+    (o * torch.tensor(do)).sum().backward()
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(g, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    B, N, H, d = 2, 19, 3, 8
+    q, k, v, do = (_rand((B, N, H, d), 20 + s) for s in range(4))
+    dq, dk, dv = attention_backward(q, k, v, do, 0.4, causal)
+    # K -> K + 1 u^T shifts every score of row i by alpha q_i.u: O is unchanged,
+    # so the gradient along that direction, sum_j dK_j, vanishes
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    # rows of P sum to one: sum_j dV_j = sum_j sum_i P_ij dO_i = sum_i dO_i
+    np.testing.assert_allclose(dv.sum(axis=1), do.sum(axis=1), atol=1e-12)
+
+
+def test_backward_constant_v_and_single_key():
+    B, N, H, d = 1, 11, 2, 4
+    q, k, do = (_rand((B, N, H, d), 30 + s) for s in range(3))
+    v = np.broadcast_to(_rand((B, 1, H, d), 33), (B, N, H, d)).copy()
+    dq, dk, dv = attention_backward(q, k, v, do, 0.5, False)
+    # every output row equals the constant row: O does not depend on Q or K
+    np.testing.assert_allclose(dq, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-12)
+    # one key: O = V_0, so dV_0 = dO_0 and dQ = dK = 0
+    q1, k1, v1, do1 = (x[:, :1] for x in (q, k, _rand((B, N, H, d), 34), do))
+    dq1, dk1, dv1 = attention_backward(q1, k1, v1, do1, 0.5, False)
+    np.testing.assert_allclose(dv1, do1, atol=1e-15)
+    np.testing.assert_allclose(dq1, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dk1, 0.0, atol=1e-15)
+
+
+def test_backward_causal_first_row_and_row_chunks():
+    B, N, H, d = 1, 29, 1, 8
+    q, k, v, do = (_rand((B, N, H, d), 40 + s) for s in range(4))
+    dq, dk, dv = attention_backward(q, k, v, do, 0.3, True)
+    # causal row 0 sees only key 0 (O_0 = V_0): its query gets no gradient
+    np.testing.assert_allclose(dq[:, 0], 0.0, atol=1e-15)
+    # the last key is seen only by the last row
+    s = 0.3 * q[0, -1, 0] @ k[0, :, 0].T
+    p_last = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+    np.testing.assert_allclose(dv[0, -1, 0], p_last[-1] * do[0, -1, 0], rtol=1e-12)
+    # chunking the rows does not change the result
+    g1 = attention_backward(q, k, v, do, 0.3, True, row_chunk=7)
+    for a, b in zip((dq, dk, dv), g1):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
