@@ -9,7 +9,7 @@ Prints ONE JSON line (metric, value, roofline, cpu_baseline, ...). Extra
 measurements (the sequence-length sweep, FP8) go to stderr, and to a JSON
 file when --out is given.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8] [--bwd]
        python bench.py --copy-calibration   (plain copy kernel for PMC scaling)
        python bench.py --gemm-ceiling       (dense bf16 GEMM reference, torch.matmul)
 """
@@ -122,6 +122,26 @@ def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
         r["hbm_GBs_cold"] = compulsory_bytes(B, N, H, d) / (msc * 1e-3) / 1e9
         r["hbm_frac_cold"] = r["hbm_GBs_cold"] / PEAK_HBM_GBS
     return r
+
+
+def bench_bwd(ea, B, N, H, d, causal, steps, warmup):
+    """attn_bwd (pre-pass + dK/dV + dQ kernels) on the forward's own O and LSE.
+    FLOPs: the pages' five products per tile pair, 2.5x the forward's count
+    (10*B*H*N^2*d, halved for causal); this implementation runs seven (it
+    recomputes S and dP in the dQ kernel)."""
+    import torch
+    q, k, v = device_inputs(B, N, H, d)
+    g = torch.Generator(device="cuda").manual_seed(1)
+    do = torch.randn(q.shape, device="cuda", generator=g).to(q.dtype)
+    o, lse = ea.attention(q, k, v, causal=causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fn = lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, causal=causal)
+    total, per = time_launches(fn, steps, warmup)
+    per_ms = sum(per) / len(per)
+    tf = 2.5 * flops(B, N, H, d, causal) / (per_ms * 1e-3) / 1e12
+    return {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "TFLOPS": tf,
+            "frac_peak": tf / PEAK_TFLOPS["bf16"]}
 
 
 def bench_fp8(ea, B, N, H, d, causal, steps, warmup):
@@ -251,6 +271,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sweep", action="store_true", help="also time the 16k-token sweep (stderr)")
     ap.add_argument("--fp8", action="store_true", help="also time the FP8 forward (stderr)")
+    ap.add_argument("--bwd", action="store_true", help="also time the backward (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -293,6 +314,15 @@ def main():
         log("long", json.dumps(r))
         rows.append(r)
         extra["sweep"] = rows
+    if args.bwd:
+        rows = []
+        for d, H in ((64, 32), (128, 16)):
+            for N in (1024, 4096, 8192):
+                for causal in (False, True):
+                    r = bench_bwd(ea, 16384 // N, N, H, d, causal, max(5, args.steps // 4), 2)
+                    log("bwd", json.dumps(r))
+                    rows.append(r)
+        extra["bwd"] = rows
     fp8_res = None
     if args.fp8:
         try:

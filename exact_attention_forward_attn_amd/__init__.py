@@ -17,11 +17,16 @@ Functions (same names as the C ABI):
 ``attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False,
 alpha=None, block_rows=128, stream=None)``
     Forward on e4m3 inputs with a bf16 output.
+``attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None)``
+    16-bit backward (d = 64 or 128): gradients dq, dk, dv of the forward's
+    O = softmax(alpha q k^T) v for an upstream gradient dout; o and lse are
+    the forward's outputs; delta is a float32 [B, H, N] workspace the call
+    fills with rowsum(dout * o).
 ``attn_last_error()``
     Message of the last failed call on this thread.
 
-Convenience wrappers that allocate the outputs with torch: ``attention`` and
-``fp8_prepare``/``attention_fp8``.
+Convenience wrappers that allocate the outputs with torch: ``attention``,
+``attention_backward`` and ``fp8_prepare``/``attention_fp8``.
 """
 from __future__ import annotations
 
@@ -30,8 +35,8 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8",
-    "attn_last_error", "attention", "fp8_prepare", "attention_fp8", "EXPORTED_SYMBOLS",
+    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd",
+    "attn_last_error", "attention", "attention_backward", "fp8_prepare", "attention_fp8", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +45,7 @@ _lib = None
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 DTYPE_BF16, DTYPE_F16 = 0, 1
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_last_error", "attn_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_last_error", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -65,6 +70,8 @@ def load():
     lib.attn_fp8_prepare.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, i, vp]
     lib.attn_fwd_fp8.restype = i
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.attn_bwd.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -164,6 +171,35 @@ def attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=Fal
                             int(bool(causal)), _default_alpha(d, alpha), _ptr(descale_q), _ptr(descale_k),
                             _ptr(descale_v), int(block_rows), _stream_handle(stream)))
     return o, lse
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None):
+    """Gradients of O = softmax(alpha q k^T) v: fills dq, dk, dv (and delta)."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, d]")
+    B, N, H, d = q.shape
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _require(t, n, q.dtype, q.shape, q.device)
+    _require(lse, "lse", torch.float32, (B, H, N), q.device)
+    _require(delta, "delta", torch.float32, (B, H, N), q.device)
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(delta), B, H, N, d, int(bool(causal)), _default_alpha(d, alpha), dt,
+                        _stream_handle(stream)))
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, o, lse, dout, causal=False, alpha=None, stream=None):
+    """Allocate dq, dk, dv and the workspace with torch and run attn_bwd."""
+    torch = _torch()
+    B, N, H, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    return attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal, alpha, stream)
 
 
 def attention(q, k, v, causal=False, alpha=None, stream=None):

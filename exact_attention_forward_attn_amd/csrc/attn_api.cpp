@@ -119,6 +119,43 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return hip_status(attn::launch_fwd_16(a, stream), "attn_fwd launch");
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, int causal, float alpha,
+             int dtype, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
+  const int s = check_shape(B, H, N, d, 2);
+  if (s == 1) return ok();
+  if (s != ATTN_OK) return s;
+  if (d == 256) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd supports d = 64 and 128 (got 256)");
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!std::isfinite(alpha) || alpha < 0.f)
+    return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
+  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+  const char* names[10] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta"};
+  for (int i = 0; i < 10; ++i) {
+    if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  const int64_t tb = (int64_t)B * N * H * d * 2;
+  const int64_t rb = (int64_t)B * H * N * 4;
+  const int64_t bytes[10] = {tb, tb, tb, tb, tb, rb, tb, tb, tb, rb};
+  // outputs (dq, dk, dv, delta) must not overlap each other or any input
+  for (int i = 6; i < 10; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (j != i && overlaps(ptrs[i], bytes[i], ptrs[j], bytes[j]))
+        return fail(ATTN_ERR_INVALID_ARG, "%s overlaps %s", names[i], names[j]);
+  attn::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal;
+  a.dtype = dtype;
+  a.scale_log2 = scale_log2(alpha);
+  a.alpha = a.scale_log2 / 1.4426950408889634f;
+  return hip_status(attn::launch_bwd_16(a, stream), "attn_bwd launch");
+}
+
 int attn_fp8_prepare(const void* x, void* x8, float* descale, int B, int H, int N, int d, int block_rows,
                      int hadamard, uint64_t hadamard_seed, void* stream) {
   const int s = check_shape(B, H, N, d, 2);

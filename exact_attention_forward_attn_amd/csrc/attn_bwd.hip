@@ -1,0 +1,504 @@
+// Exact attention backward for 16-bit inputs on gfx950 (MI355X).
+//
+// What is computed ("FlashAttention-3 on Hopper", chapter 7, section 7.1):
+// for S = alpha Q K^T, P = softmax(S), O = P V and an upstream gradient dO,
+//   D_i = rowsum(dO_i o O_i)                   (section 7.1.2)
+//   P   = 2^(S log2(e) - LSE_i log2(e))        (section 7.1.3: no running max)
+//   dV  = P^T dO,   dP = dO V^T,   dS = P o (dP - D)
+//   dQ  = alpha dS K,   dK = alpha dS^T Q      (alpha applied once, at the end,
+//                                               section 7.1.5)
+//
+// Three kernels:
+// * pre_kernel: D (HBM-bound, one 16-byte load per operand and lane).
+// * dkdv_kernel: KV-parallel (section 7.2): a workgroup owns 128 keys (32 per
+//   wave) of one head and loops over 32-query tiles of Q and dO staged in
+//   LDS; dK^T and dV^T stay in registers. With the wave's keys as the B
+//   operand, S = Q K^T and dP = dO V^T come out with a lane owning one key
+//   column, so the converted P and dS registers are directly the B operands
+//   of dV^T += dO^T P and dK^T += Q^T dS, whose A operands come from the Q and
+//   dO tiles through the transposing LDS read (the contraction runs over the
+//   queries in the accumulator's row order, as the forward's P V does over
+//   keys).
+// * dq_kernel: query-parallel, the forward's structure without the online
+//   softmax: S^T = K Q^T and dP^T = V dO^T with a lane owning one query, then
+//   dQ^T += K^T dS^T. This is the pages' "second kernel that recomputes the
+//   intermediates" option for the dQ reduction (section 7.2.3): it costs two
+//   extra products per tile but needs no atomics or fp32 dQ buffer and is
+//   deterministic.
+// Causal masking follows section 7.2.2: a key block only meets query rows at
+// or below its first key, so the query loop of dkdv_kernel starts there.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_internal.h"
+#include "kernel_common.h"
+
+namespace attn {
+namespace bwd16 {
+
+using namespace attn::dev;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- D = rowsum(dO o O) ------------------------------------------------------
+// rows in memory order r = (b*N + n)*H + h; D_i is stored as delta[(b*H + h)*N + n]
+template <int D, typename T>
+__global__ __launch_bounds__(256) void pre_kernel(const T* o, const T* dout, float* delta, int B, int H, int N) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int LPR = D / 8;       // lanes per row, 8 elements each
+  constexpr int RPB = 256 / LPR;   // rows per workgroup
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int li = threadIdx.x % LPR;
+  const int64_t nrows = (int64_t)B * N * H;
+  float acc = 0.f;
+  if (row < nrows) {
+    typedef T t8 __attribute__((ext_vector_type(8)));
+    const t8 x = __builtin_bit_cast(t8, *(const u32x4*)(o + row * D + 8 * li));
+    const t8 y = __builtin_bit_cast(t8, *(const u32x4*)(dout + row * D + 8 * li));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < nrows && li == 0) {
+    const int64_t h = row % H, bn = row / H;
+    const int64_t n = bn % N, b = bn / N;
+    delta[(b * H + h) * N + n] = acc;
+  }
+#endif
+}
+
+struct KernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, N;
+  int n_blk;      // ceil(N / 128)
+  float c;        // alpha * log2(e)
+  float alpha;
+};
+
+// waves per SIMD each kernel is compiled for (its register budget): dK/dV
+// keeps K, V, dK^T and dV^T in registers
+template <int D>
+constexpr int kWavesDkdv = D == 64 ? 2 : 1;
+template <int D>
+constexpr int kWavesDq = D == 256 ? 1 : 2;
+
+// Per-lane LDS offsets shared by both kernels for 32-row tiles stored with the
+// K-style swizzle (they are read row-wise as MFMA A operands and, for the
+// transposed operands, through ds_read_b64_tr_b16).
+template <int D>
+struct TileOffsets {
+  typedef Geo<D, 1> G;
+  static constexpr int KC = D / 16;
+  static constexpr int KCL = KC < 8 ? KC : 8;
+  static constexpr int DB = D / 32;
+  static constexpr int DBL = DB < 4 ? DB : 4;
+  static constexpr int KGP = (G::RPS * 4) % 16 == 0 ? 1 : 2;
+  uint32_t cg[KGP];     // global -> LDS copy: per-lane byte offset of segment t
+  int rofs[KCL];        // row reads: row l32, logical chunk 2kc + h32
+  int tlo[DBL], thi[DBL];  // transposing reads: rows r0 and r0 + 8
+  __device__ __forceinline__ void init(int lane, int wave, uint32_t RS) {
+    const int h32 = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int t = 0; t < KGP; ++t) {
+      const int r = (wave + 4 * t) * G::RPS + lane / G::CPR;
+      const int pc = lane % G::CPR;
+      cg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * 4 * G::RPS * RS;
+    }
+#pragma unroll
+    for (int i = 0; i < KCL; ++i) rofs[i] = l32 * G::ROWB + (((2 * i + h32) ^ swz_k<D>(l32)) << 4);
+    // 16-lane group g = lane/16, piece p = lane%16: row 4*h32 + p/4 (+8 for the
+    // second read), dims db*32 + 16*(g%2) + 4*(p%4)
+    const int p = lane & 15, dh = (lane >> 4) & 1;
+    const int r0 = 4 * h32 + (p >> 2);
+#pragma unroll
+    for (int i = 0; i < DBL; ++i) {
+      const int ch = 4 * i + 2 * dh + ((p & 3) >> 1);
+      tlo[i] = r0 * G::ROWB + ((ch ^ swz_k<D>(r0)) << 4) + 8 * (p & 1);
+      thi[i] = (r0 + 8) * G::ROWB + ((ch ^ swz_k<D>(r0 + 8)) << 4) + 8 * (p & 1);
+    }
+  }
+};
+
+// Copy 32 rows starting at row0 of one head into an LDS tile (K-style swizzle).
+template <int D>
+__device__ __forceinline__ void copy_tile(const TileOffsets<D>& to, const __amdgpu_buffer_rsrc_t& rs, char* dst,
+                                          int wave, int row0, uint32_t RS) {
+  typedef Geo<D, 1> G;
+  const uint32_t base = (uint32_t)row0 * RS;
+#pragma unroll
+  for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
+    const uint32_t voff = to.cg[(t & 1) % TileOffsets<D>::KGP] + (base + (uint32_t)t * 4 * G::RPS * RS);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + 4 * t) * 1024), 16, voff, 0, 0, 0);
+  }
+}
+
+// A operand of row-read tile rows (32 rows x 16 dims, step kc)
+template <int D, typename T>
+__device__ __forceinline__ typename Elt<T>::v8 row_op(const TileOffsets<D>& to, const char* tile, int kc) {
+  return *(const typename Elt<T>::v8*)(tile + (kc / 8) * 256 + to.rofs[kc % 8]);
+}
+// A operand of the transposed tile: 32 dims (block db) x 16 rows (chunk ks)
+template <int D, typename T>
+__device__ __forceinline__ typename Elt<T>::v8 tr_op(const TileOffsets<D>& to, const char* tile, int db, int ks) {
+  typedef Elt<T> E;
+  const LDS_AS char* base = (const LDS_AS char*)tile + 16 * ks * Geo<D, 1>::ROWB + (db / 4) * 256;
+  const typename E::v4 lo = E::tr_read(base + to.tlo[db % 4]);
+  const typename E::v4 hi = E::tr_read(base + to.thi[db % 4]);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void barrier_all() {
+  wait_lgkmcnt0();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// B operand registers of a row of one head: dims 16kc + 8*h32 .. +7
+template <int D, typename T>
+__device__ __forceinline__ void load_row_operand(const __amdgpu_buffer_rsrc_t& rs, uint32_t row, uint32_t RS, int h32,
+                                                 typename Elt<T>::v8 (&reg)[D / 16]) {
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rs, row * RS + (16 * kc + 8 * h32) * 2, 0, 0);
+    reg[kc] = __builtin_bit_cast(typename Elt<T>::v8, raw);
+  }
+}
+
+// Store an accumulator of dims x rows (lane = row l32) as row `row` of one
+// head, scaled by f.
+template <int D, typename T>
+__device__ __forceinline__ void store_rows(T* head, int row, uint32_t RS_elems, int h32, const f32x16 (&acc)[D / 32],
+                                           float f) {
+  T* rp = head + (int64_t)row * RS_elems;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef T t4 __attribute__((ext_vector_type(4)));
+      float __attribute__((ext_vector_type(4))) x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * f;
+      t4 ov = __builtin_convertvector(x, t4);
+      *(u32x2*)(rp + db * 32 + 8 * g + 4 * h32) = __builtin_bit_cast(u32x2, ov);
+    }
+}
+
+// Two 16-bit B operands (rows 0-7 and 8-15 of the accumulator) from 16 floats.
+template <typename T>
+__device__ __forceinline__ void pack16(const float (&x)[16], typename Elt<T>::v8 (&out)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    f32x8 f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = x[8 * ks + e];
+    out[ks] = __builtin_convertvector(f, typename Elt<T>::v8);
+  }
+}
+
+// ---- dK, dV: KV-parallel ---------------------------------------------------------
+template <int D, bool CAUSAL, typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesDkdv<D>, kWavesDkdv<D>)))
+void dkdv_kernel(KernelArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef Elt<T> E;
+  typedef typename E::v8 v8;
+  typedef Geo<D, 1> G;
+  typedef TileOffsets<D> TO;
+  constexpr int KC = D / 16;
+  constexpr int DB = D / 32;
+
+  __shared__ __attribute__((aligned(1024))) char qbuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char obuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char obuf1[G::TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h32 = lane >> 5, l32 = lane & 31;
+
+  // key blocks: causal grids go from the first block (the longest query
+  // range) to the last
+  const int BH = a.B * a.H;
+  int kblk, bh;
+  decode_block(blockIdx.x, a.n_blk, BH, CAUSAL, kblk, bh);
+  if (CAUSAL) kblk = a.n_blk - 1 - kblk;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int N = a.N;
+  const int k0 = kblk * 128;
+  const int key = k0 + 32 * wave + l32;   // this lane's key (column of S)
+  const uint32_t RS = (uint32_t)a.H * D * 2;
+  const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;
+  const uint32_t span = (uint32_t)(N - 1) * RS + D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + head_off, span);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + head_off, span);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + head_off, span);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.dout + head_off, span);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (int64_t)bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (int64_t)bh * N, (uint32_t)N * 4);
+
+  v8 kreg[KC], vreg[KC];
+  load_row_operand<D, T>(rk, (uint32_t)key, RS, h32, kreg);
+  load_row_operand<D, T>(rv, (uint32_t)key, RS, h32, vreg);
+  TO to;
+  to.init(lane, wave, RS);
+
+  f32x16 dkt[DB], dvt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkt[db] = f32x16{};
+    dvt[db] = f32x16{};
+  }
+  const float c = a.c;
+
+  // LSE and D of the 16 query rows a lane holds in a tile: rows 8g + 4*h32 +
+  // 0..3 of the tile for g = 0..3 (dword loads: rows past N read as 0 one by
+  // one, and those rows are masked anyway)
+  auto load_rows = [&](int q0t, f32x4 (&l2)[4], f32x4 (&dl)[4]) ATTN_INLINE {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t off = (uint32_t)(q0t + 8 * g + 4 * h32 + e) * 4;
+        l2[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0));
+        dl[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off, 0, 0));
+      }
+  };
+
+  const int nqt = (N + 31) / 32;
+  const int t0 = CAUSAL ? k0 / 32 : 0;   // query rows below k0 meet none of these keys
+
+  auto compute = [&](const char* qt, const char* ot, int q0t, const f32x4 (&l2)[4], const f32x4 (&dl)[4]) ATTN_INLINE {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) s = E::mfma(row_op<D, T>(to, qt, kc), kreg[kc], s);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) dp = E::mfma(row_op<D, T>(to, ot, kc), vreg[kc], dp);
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = q0t + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      const bool ok = qr < N && key < N && (!CAUSAL || key <= qr);
+      const float lse = l2[r >> 2][r & 3];
+      // a row with LSE = -inf has no keys; its p stays 0
+      const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(s[r], c, -lse * kLog2e)) : 0.f;
+      pv[r] = p;
+      dsv[r] = p * (dp[r] - dl[r >> 2][r & 3]);
+    }
+    v8 pk[2], dk8[2];
+    pack16<T>(pv, pk);
+    pack16<T>(dsv, dk8);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dvt[db] = E::mfma(tr_op<D, T>(to, ot, db, ks), pk[ks], dvt[db]);
+        dkt[db] = E::mfma(tr_op<D, T>(to, qt, db, ks), dk8[ks], dkt[db]);
+      }
+  };
+
+  f32x4 l2c[4], dlc[4], l2n[4], dln[4];
+  if (t0 < nqt) {
+    copy_tile<D>(to, rq, qbuf0, wave, 32 * t0, RS);
+    copy_tile<D>(to, ro, obuf0, wave, 32 * t0, RS);
+    load_rows(32 * t0, l2c, dlc);
+    wait_vmcnt<0>();
+    barrier_all();
+  }
+  // slot of tile t is (t - t0) % 2; the loop is unrolled by two so that both
+  // slots are compile-time objects
+  auto step = [&](int t, auto j_tag) ATTN_INLINE {
+    constexpr int J = decltype(j_tag)::value;
+    char* qcur = J ? qbuf1 : qbuf0;
+    char* ocur = J ? obuf1 : obuf0;
+    char* qnxt = J ? qbuf0 : qbuf1;
+    char* onxt = J ? obuf0 : obuf1;
+    if (t + 1 < nqt) {
+      copy_tile<D>(to, rq, qnxt, wave, 32 * (t + 1), RS);
+      copy_tile<D>(to, ro, onxt, wave, 32 * (t + 1), RS);
+      load_rows(32 * (t + 1), l2n, dln);
+    }
+    compute(qcur, ocur, 32 * t, l2c, dlc);
+    wait_vmcnt<0>();
+    barrier_all();
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l2c[g] = l2n[g];
+      dlc[g] = dln[g];
+    }
+  };
+  int t = t0;
+  for (; t + 1 < nqt; t += 2) {
+    step(t, Int<0>{});
+    step(t + 1, Int<1>{});
+  }
+  if (t < nqt) step(t, Int<0>{});
+
+  if (key < N) {
+    store_rows<D, T>((T*)a.dk + head_off, key, (uint32_t)a.H * D, h32, dkt, a.alpha);
+    store_rows<D, T>((T*)a.dv + head_off, key, (uint32_t)a.H * D, h32, dvt, 1.0f);
+  }
+#endif
+}
+
+// ---- dQ: query-parallel ----------------------------------------------------------
+template <int D, bool CAUSAL, typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesDq<D>, kWavesDq<D>)))
+void dq_kernel(KernelArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef Elt<T> E;
+  typedef typename E::v8 v8;
+  typedef Geo<D, 1> G;
+  typedef TileOffsets<D> TO;
+  constexpr int KC = D / 16;
+  constexpr int DB = D / 32;
+
+  __shared__ __attribute__((aligned(1024))) char kbuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[G::TILE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h32 = lane >> 5, l32 = lane & 31;
+
+  const int BH = a.B * a.H;
+  int mblk, bh;
+  decode_block(blockIdx.x, a.n_blk, BH, CAUSAL, mblk, bh);
+  const int b = bh / a.H, hh = bh % a.H;
+  const int N = a.N;
+  const int q0 = mblk * 128;
+  const int qi = q0 + 32 * wave + l32;    // this lane's query (column of S^T)
+  const uint32_t RS = (uint32_t)a.H * D * 2;
+  const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;
+  const uint32_t span = (uint32_t)(N - 1) * RS + D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + head_off, span);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + head_off, span);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + head_off, span);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.dout + head_off, span);
+
+  v8 qreg[KC], oreg[KC];
+  load_row_operand<D, T>(rq, (uint32_t)qi, RS, h32, qreg);
+  load_row_operand<D, T>(ro, (uint32_t)qi, RS, h32, oreg);
+  TO to;
+  to.init(lane, wave, RS);
+  const float lse = qi < N ? a.lse[(int64_t)bh * N + qi] : 0.f;
+  const float dl = qi < N ? a.delta[(int64_t)bh * N + qi] : 0.f;
+  const bool live = lse != -__builtin_inff();
+  const float l2 = live ? lse * kLog2e : 0.f;
+
+  f32x16 dqt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
+  const float c = a.c;
+
+  const int kv_end = CAUSAL ? min(N, q0 + 128) : N;
+  const int nkt = (kv_end + 31) / 32;
+
+  auto compute = [&](const char* kt, const char* vt, int kv0) ATTN_INLINE {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) s = E::mfma(row_op<D, T>(to, kt, kc), qreg[kc], s);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) dp = E::mfma(row_op<D, T>(to, vt, kc), oreg[kc], dp);
+    float dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = kv0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+      const bool ok = live && kr < N && (!CAUSAL || kr <= qi);
+      const float p = ok ? exp2_fast(__builtin_fmaf(s[r], c, -l2)) : 0.f;
+      dsv[r] = p * (dp[r] - dl);
+    }
+    v8 dk8[2];
+    pack16<T>(dsv, dk8);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dqt[db] = E::mfma(tr_op<D, T>(to, kt, db, ks), dk8[ks], dqt[db]);
+  };
+
+  if (nkt > 0) {
+    copy_tile<D>(to, rk, kbuf0, wave, 0, RS);
+    copy_tile<D>(to, rv, vbuf0, wave, 0, RS);
+    wait_vmcnt<0>();
+    barrier_all();
+  }
+  auto step = [&](int t, auto j_tag) ATTN_INLINE {
+    constexpr int J = decltype(j_tag)::value;
+    char* kcur = J ? kbuf1 : kbuf0;
+    char* vcur = J ? vbuf1 : vbuf0;
+    char* knxt = J ? kbuf0 : kbuf1;
+    char* vnxt = J ? vbuf0 : vbuf1;
+    if (t + 1 < nkt) {
+      copy_tile<D>(to, rk, knxt, wave, 32 * (t + 1), RS);
+      copy_tile<D>(to, rv, vnxt, wave, 32 * (t + 1), RS);
+    }
+    compute(kcur, vcur, 32 * t);
+    wait_vmcnt<0>();
+    barrier_all();
+  };
+  int t = 0;
+  for (; t + 1 < nkt; t += 2) {
+    step(t, Int<0>{});
+    step(t + 1, Int<1>{});
+  }
+  if (t < nkt) step(t, Int<0>{});
+
+  if (qi < N) store_rows<D, T>((T*)a.dq + head_off, qi, (uint32_t)a.H * D, h32, dqt, a.alpha);
+#endif
+}
+
+template <int D, typename T>
+int launch_d(const BwdArgs& f, hipStream_t st) {
+  {
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t rows = (int64_t)f.B * f.N * f.H;
+    const int grid = (int)((rows + RPB - 1) / RPB);
+    hipLaunchKernelGGL((pre_kernel<D, T>), dim3(grid), dim3(256), 0, st, (const T*)f.o, (const T*)f.dout, f.delta,
+                       f.B, f.H, f.N);
+  }
+  KernelArgs a;
+  a.q = f.q; a.k = f.k; a.v = f.v; a.dout = f.dout; a.lse = f.lse; a.delta = f.delta;
+  a.dq = f.dq; a.dk = f.dk; a.dv = f.dv;
+  a.B = f.B; a.H = f.H; a.N = f.N;
+  a.n_blk = (f.N + 127) / 128;
+  a.c = f.scale_log2;
+  a.alpha = f.alpha;
+  const int grid = a.n_blk * f.B * f.H;
+  if (f.causal) {
+    hipLaunchKernelGGL((dkdv_kernel<D, true, T>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dq_kernel<D, true, T>), dim3(grid), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((dkdv_kernel<D, false, T>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dq_kernel<D, false, T>), dim3(grid), dim3(256), 0, st, a);
+  }
+  return (int)hipGetLastError();
+}
+
+template <typename T>
+int dispatch(const BwdArgs& f, hipStream_t st) {
+  switch (f.d) {
+    case 64: return launch_d<64, T>(f, st);
+    case 128: return launch_d<128, T>(f, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace bwd16
+
+int launch_bwd_16(const BwdArgs& f, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  return f.dtype == 0 ? bwd16::dispatch<__bf16>(f, st) : bwd16::dispatch<_Float16>(f, st);
+}
+
+}  // namespace attn

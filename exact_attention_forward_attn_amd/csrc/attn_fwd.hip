@@ -50,80 +50,6 @@ namespace fwd16 {
 
 using namespace attn::dev;
 
-template <typename T>
-struct Elt;
-
-template <>
-struct Elt<__bf16> {
-  typedef bf16x8 v8;
-  typedef bf16x4 v4;
-  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ v4 tr_read(const LDS_AS char* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS v4*)p);
-  }
-  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
-  // two floats rounded (to nearest even) to one packed 16-bit pair
-  static __device__ __forceinline__ v2 cvt2(float a, float b) {
-    const float __attribute__((ext_vector_type(2))) f = {a, b};
-    return __builtin_convertvector(f, v2);
-  }
-  // acc + x.x + x.y, summed in float32 (v_dot2 against (1, 1))
-  static __device__ __forceinline__ float dot2(v2 x, float acc) {
-    const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
-  }
-};
-
-template <>
-struct Elt<_Float16> {
-  typedef f16x8 v8;
-  typedef f16x4 v4;
-  static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  typedef __fp16 raw4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
-  static __device__ __forceinline__ v4 tr_read(const LDS_AS char* p) {
-    return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((LDS_AS raw4*)p));
-  }
-  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
-  static __device__ __forceinline__ v2 cvt2(float a, float b) {
-    const float __attribute__((ext_vector_type(2))) f = {a, b};
-    return __builtin_convertvector(f, v2);
-  }
-  static __device__ __forceinline__ float dot2(v2 x, float acc) {
-    const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(x, one, acc, false);
-  }
-};
-
-// Geometry of the K/V tiles in LDS for head dimension D.
-template <int D, int KB>
-struct Geo {
-  static constexpr int BN = 32 * KB;                // keys per KV tile
-  static constexpr int ROWB = D * 2;                // bytes per key row
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  static constexpr int TILE = BN * ROWB;            // bytes of one K or V tile
-  static constexpr int STAGE = 2 * TILE;            // K tile then V tile
-  static constexpr int SEGS = TILE / 1024;          // 1 KiB copy segments per tile
-  static constexpr int RPS = 1024 / ROWB;           // rows per segment
-  static constexpr int SEG_PER_WAVE = SEGS / 4;
-  static_assert(SEGS % 4 == 0, "tile must split evenly over 4 waves");
-};
-
-// XOR swizzles of the 16-byte chunk index of LDS row r. K rows are read 32
-// rows x one chunk at a time (A operand of S^T); V rows are read through the
-// transposing load, 4 rows x 4 chunks per 16 lanes.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return swz_rows<2 * D>(r);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int r) {
-  return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
-}
-
 #ifndef ATTN_DS_LEAD
 #define ATTN_DS_LEAD 2
 #endif

@@ -23,6 +23,24 @@ struct FwdArgs {
   float scale_log2;  // alpha * log2(e), clamped to >= 1e-30
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;
+  int B, H, N, d;
+  int causal;
+  int dtype;
+  float alpha;       // alpha, clamped to >= 1e-30 / log2(e)
+  float scale_log2;  // alpha * log2(e), clamped to >= 1e-30
+};
+
 struct PrepArgs {
   const void* x;
   void* x8;
@@ -37,6 +55,7 @@ struct PrepArgs {
 int launch_fwd_16(const FwdArgs& a, void* stream);
 int launch_fwd_fp8(const FwdArgs& a, void* stream);
 int launch_fp8_prepare(const PrepArgs& a, void* stream);
+int launch_bwd_16(const BwdArgs& a, void* stream);
 const char* hip_error_name(int err);
 
 }  // namespace attn

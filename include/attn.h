@@ -131,6 +131,33 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
                  const float* descale_q, const float* descale_k, const float* descale_v,
                  int block_rows, void* stream);
 
+/*
+ * attn_bwd -- gradients of the exact attention forward ("FlashAttention-3 on
+ * Hopper", chapter 7, section 7.1): for O = softmax(alpha Q K^T) V and an
+ * upstream gradient dO,
+ *   D_i = rowsum(dO_i o O_i)            (section 7.1.2, written to delta)
+ *   P   = exp(alpha Q K^T - LSE)        (section 7.1.3, recomputed, never stored)
+ *   dV  = P^T dO,  dP = dO V^T,  dS = P o (dP - D)
+ *   dQ  = alpha dS K,  dK = alpha dS^T Q.
+ *
+ *   q, k, v, o, dout  [B, N, H, d], dtype as attn_fwd (o and lse are the
+ *            forward's outputs for the same q, k, v, causal, alpha).
+ *   lse      [B, H, N] float32 from attn_fwd.
+ *   dq, dk, dv  [B, N, H, d] outputs in the input dtype (device memory).
+ *   delta    [B, H, N] float32 workspace owned by the caller; the call writes
+ *            D into it (no allocation inside the library).
+ *   d        64 or 128 (d = 256 returns ATTN_ERR_UNSUPPORTED).
+ *   Other arguments and the error behaviour as attn_fwd. dq, dk, dv and delta
+ *   must not overlap each other or the inputs.
+ *
+ * dQ comes from a second, query-parallel kernel that recomputes P and dP
+ * (one of the pages' options for the dQ reduction, section 7.2.3), so no
+ * atomics are used and the result is deterministic.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, int causal, float alpha,
+             int dtype, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */
 const char* attn_last_error(void);

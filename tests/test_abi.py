@@ -124,6 +124,38 @@ def test_fp8_forward_rejects_bad_arguments(kw, status, msg):
     assert msg in ea.attn_last_error()
 
 
+def _bwd(**kw):
+    lib = ea.load()
+    names = ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")
+    a = {n: FAKE + i * 0x10000000 for i, n in enumerate(names)}
+    a.update(dict(B=1, H=2, N=256, d=64, causal=0, alpha=0.125, dtype=0, stream=None))
+    a.update(kw)
+    return lib.attn_bwd(*(a[n] for n in names), a["B"], a["H"], a["N"], a["d"], a["causal"], a["alpha"],
+                        a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=256), ea.ATTN_ERR_UNSUPPORTED, "d = 64 and 128"),
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(dtype=3), ea.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(dout=None), ea.ATTN_ERR_INVALID_ARG, "dout is null"),
+    (dict(delta=None), ea.ATTN_ERR_INVALID_ARG, "delta is null"),
+    (dict(dk=FAKE + 0x70000000 + 4), ea.ATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(dq=FAKE), ea.ATTN_ERR_INVALID_ARG, "dq overlaps q"),
+    (dict(delta=FAKE + 0x80000000 + 64), ea.ATTN_ERR_INVALID_ARG, "dv overlaps delta"),
+    (dict(causal=3), ea.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(alpha=-1.0), ea.ATTN_ERR_INVALID_ARG, "alpha"),
+])
+def test_bwd_rejects_bad_arguments_before_launch(kw, status, msg):
+    assert _bwd(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    assert _bwd(N=0) == ea.ATTN_OK
+    assert _bwd(B=0) == ea.ATTN_OK
+
+
 def test_binding_has_no_cpu_fallback(monkeypatch):
     # with the library path pointing nowhere the binding must raise, not compute
     monkeypatch.setattr(ea, "lib_path", "/nonexistent/libattn.so")

@@ -1,0 +1,95 @@
+"""GPU parity of the 16-bit backward (attn_bwd) against the float64 oracle.
+
+Inputs: Q, K, V from ``synth_inputs.make_qkv`` and dO from ``make_dout``
+(N(0,1) rounded to bf16); O and LSE come from the library's own forward, as a
+training step would pass them. The oracle recomputes everything in float64
+from the same rounded Q, K, V, dO.
+
+Tolerances (derived from the arithmetic: P, dS and the outputs are rounded to
+16 bits, 2^-9 relative each; sums are float32; D is formed from the 16-bit
+O): per gradient, max |g - g_ref| <= 2e-2 * max |g_ref| and
+rms(g - g_ref) <= 1e-2 * rms(g_ref).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_util import device_qkv, to_f64
+from oracle.attention_bwd import attention_backward
+from synth_inputs import make_dout
+
+REL_MAX = 2e-2
+REL_RMS = 1e-2
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(ea, B, N, H, d, causal, seed=0, dtype="bf16", alpha=None):
+    import torch
+    (q, k, v), vals = device_qkv(B, N, H, d, seed=seed, dtype=dtype)
+    bits, do_vals = make_dout(B, N, H, d, seed=seed, dtype=dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    do = torch.from_numpy(bits.view(np.int16)).view(tdt).cuda()
+    o, lse = ea.attention(q, k, v, causal=causal, alpha=alpha)
+    dq, dk, dv = ea.attention_backward(q, k, v, o, lse, do, causal=causal, alpha=alpha)
+    torch.cuda.synchronize()
+    return (dq, dk, dv), vals, do_vals, (q, k, v, o, lse, do)
+
+
+def _rel(g, ref):
+    scale_max = float(np.abs(ref).max()) or 1.0
+    scale_rms = float(math.sqrt(np.mean(ref ** 2))) or 1.0
+    diff = g - ref
+    return {"rel_max": float(np.abs(diff).max()) / scale_max,
+            "rel_rms": float(math.sqrt(np.mean(diff ** 2))) / scale_rms}
+
+
+def _check(grads, vals, do_vals, causal, alpha=None, tag=""):
+    refs = attention_backward(*vals, do_vals, alpha, causal)
+    for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+        e = _rel(to_f64(g), r)
+        assert np.isfinite(to_f64(g)).all(), (tag, name)
+        assert e["rel_max"] <= REL_MAX and e["rel_rms"] <= REL_RMS, (tag, name, e)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 129, 300])
+def test_bwd_small_shapes(gpu, d, causal, N):
+    grads, vals, do_vals, _ = _run(gpu, 2, N, 2, d, causal, seed=N)
+    _check(grads, vals, do_vals, causal, tag=(d, causal, N))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_several_tiles(gpu, causal):
+    # 1024 queries and keys: 8 key blocks of 128, 32 query tiles of 32
+    grads, vals, do_vals, _ = _run(gpu, 1, 1024, 2, 128, causal, seed=5)
+    _check(grads, vals, do_vals, causal, tag=("n1024", causal))
+
+
+def test_bwd_f16_and_alpha(gpu):
+    grads, vals, do_vals, _ = _run(gpu, 1, 200, 2, 64, True, seed=7, dtype="f16", alpha=0.3)
+    _check(grads, vals, do_vals, True, alpha=0.3, tag="f16")
+
+
+def test_bwd_delta_is_rowsum_of_dout_times_o(gpu):
+    import torch
+    _, _, _, (q, k, v, o, lse, do) = _run(gpu, 1, 77, 3, 64, False, seed=9)
+    B, N, H, d = q.shape
+    delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    gpu.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, delta)
+    torch.cuda.synchronize()
+    ref = np.einsum("bnhd,bnhd->bhn", to_f64(do), to_f64(o))
+    np.testing.assert_allclose(to_f64(delta), ref, rtol=1e-5, atol=1e-5)
+
+
+def test_bwd_is_deterministic(gpu):
+    import torch
+    g1, _, _, t = _run(gpu, 1, 300, 2, 128, True, seed=11)
+    q, k, v, o, lse, do = t
+    g2 = gpu.attention_backward(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
