@@ -18,10 +18,12 @@ attention_bwd  gradients dQ, dK, dV of the plain definition.
 fp8         Sylvester Hadamard matrix, fast Walsh-Hadamard transform, the
             splitmix64 sign generator, OCP e4m3 encode/decode, block
             quantisation, and the fp8-emulating reference.
+variants    grouped/multi-query heads, N_q != N_k, packed variable-length
+            batches, split-KV partial states and their merge.
 
 Every function names the passage of the pages it follows. Pins (tests that
 check the oracle against something other than itself) live in
-``tests/test_oracle.py``, ``tests/test_oracle_bwd.py`` and
-``tests/test_oracle_fp8.py``.
+``tests/test_oracle.py``, ``tests/test_oracle_bwd.py``,
+``tests/test_oracle_fp8.py`` and ``tests/test_oracle_variants.py``.
 """
-from . import attention, attention_bwd, fp8  # noqa: F401
+from . import attention, attention_bwd, fp8, variants  # noqa: F401
