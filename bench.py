@@ -9,7 +9,7 @@ Prints ONE JSON line (metric, value, roofline, cpu_baseline, ...). Extra
 measurements (the sequence-length sweep, FP8) go to stderr, and to a JSON
 file when --out is given.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8] [--bwd]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8] [--bwd] [--decode]
        python bench.py --copy-calibration   (plain copy kernel for PMC scaling)
        python bench.py --gemm-ceiling       (dense bf16 GEMM reference, torch.matmul)
 """
@@ -92,12 +92,14 @@ _FLUSH_BUF = None
 
 
 def mall_flush():
-    """Writes 512 MiB (twice the 256 MB MALL) so the next launch reads HBM."""
+    """Reads 512 MiB (twice the 256 MB MALL) so the next launch reads HBM.
+    (A read, not a write: written lines would still be draining to HBM while
+    the timed kernel runs.)"""
     global _FLUSH_BUF
     import torch
     if _FLUSH_BUF is None:
-        _FLUSH_BUF = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    _FLUSH_BUF.fill_(1)
+        _FLUSH_BUF = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    _FLUSH_BUF.max()
 
 
 def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
@@ -142,6 +144,48 @@ def bench_bwd(ea, B, N, H, d, causal, steps, warmup):
     tf = 2.5 * flops(B, N, H, d, causal) / (per_ms * 1e-3) / 1e12
     return {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "TFLOPS": tf,
             "frac_peak": tf / PEAK_TFLOPS["bf16"]}
+
+
+def decode_bytes(B, Hq, Hkv, Nk, d):
+    """Compulsory bytes of one decode step: the K/V cache read once, one
+    query row per head read and one output row written (16-bit), LSE."""
+    return 4.0 * B * Nk * Hkv * d + 4.0 * B * Hq * d + 4.0 * B * Hq
+
+
+def bench_decode(ea, B, Hq, Hkv, Nk, d, splits, steps, warmup):
+    """attn_fwd_ex with one query per sequence against an Nk-key cache
+    (grouped heads packed into one tile, split-KV + combine). HBM-bound: the
+    cache is evicted from the MALL before each timed launch."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn((B, 1, Hq, d), device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn((B, Nk, Hkv, d), device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn((B, Nk, Hkv, d), device="cuda", generator=g).to(torch.bfloat16)
+    if splits is None:
+        splits = ea.attn_num_splits_heuristic(B, Hq, Hkv, 1, Nk, d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, 1), dtype=torch.float32, device="cuda")
+    nb = ea.attn_splitkv_workspace_bytes(splits, B, Hq, d)
+    ws = torch.empty(max(nb // 4, 4), dtype=torch.float32, device="cuda")
+    fn = lambda: ea.attn_fwd_ex(q, k, v, o, lse, causal=True, num_splits=splits, workspace=ws)
+    _, per = time_launches(fn, steps, warmup, flush=mall_flush)
+    ms = sum(per) / len(per)
+    gbs = decode_bytes(B, Hq, Hkv, Nk, d) / (ms * 1e-3) / 1e9
+    return {"B": B, "Hq": Hq, "Hkv": Hkv, "Nk": Nk, "d": d, "splits": splits, "ms": ms, "hbm_GBs": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS}
+
+
+def hbm_read_ceiling():
+    """Plain streaming reads on this part: torch's max over 1 GiB (read-only)
+    and a 1 GiB device copy (read + write), with the MALL flushed first."""
+    import torch
+    x = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    _, per = time_launches(lambda: x.max(), 10, 2, flush=mall_flush)
+    ms_r = sum(per) / len(per)
+    _, per = time_launches(lambda: y.copy_(x), 10, 2, flush=mall_flush)
+    ms_c = sum(per) / len(per)
+    return {"read_GBs": (1 << 30) / (ms_r * 1e-3) / 1e9, "copy_GBs": 2 * (1 << 30) / (ms_c * 1e-3) / 1e9}
 
 
 def bench_fp8(ea, B, N, H, d, causal, steps, warmup):
@@ -272,6 +316,7 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time the 16k-token sweep (stderr)")
     ap.add_argument("--fp8", action="store_true", help="also time the FP8 forward (stderr)")
     ap.add_argument("--bwd", action="store_true", help="also time the backward (stderr)")
+    ap.add_argument("--decode", action="store_true", help="also time split-KV decode (stderr)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -323,6 +368,21 @@ def main():
                     log("bwd", json.dumps(r))
                     rows.append(r)
         extra["bwd"] = rows
+    if args.decode:
+        rows = []
+        for Nk in (1024, 4096, 8192, 32768):
+            for splits in (1, None):
+                r = bench_decode(ea, 8, 64, 8, Nk, 128, splits, max(10, args.steps), 3)
+                log("decode", json.dumps(r))
+                rows.append(r)
+        for B, Hq, Hkv in ((1, 32, 8), (32, 32, 8), (16, 16, 16), (64, 8, 8)):
+            r = bench_decode(ea, B, Hq, Hkv, 8192, 128, None, max(10, args.steps), 3)
+            log("decode", json.dumps(r))
+            rows.append(r)
+        ceil = hbm_read_ceiling()
+        log("hbm_read_ceiling", json.dumps(ceil))
+        extra["decode"] = rows
+        extra["hbm_read_ceiling"] = ceil
     fp8_res = None
     if args.fp8:
         try:

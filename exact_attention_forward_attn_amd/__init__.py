@@ -22,11 +22,20 @@ alpha=None, block_rows=128, stream=None)``
     O = softmax(alpha q k^T) v for an upstream gradient dout; o and lse are
     the forward's outputs; delta is a float32 [B, H, N] workspace the call
     fills with rowsum(dout * o).
+``attn_fwd_ex(q, k, v, o, lse, causal=False, alpha=None, cu_seqlens_q=None, cu_seqlens_k=None,
+max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, workspace=None, stream=None)``
+    16-bit forward with Hq query heads over Hkv key/value heads, N_q != N_k,
+    packed variable-length batches (int32 cu_seqlens) and split-KV. Dense:
+    q, o [B, Nq, Hq, d], k, v [B, Nk, Hkv, d], lse [B, Hq, Nq]. Packed:
+    q, o [total_q, Hq, d], k, v [total_k, Hkv, d], lse [Hq, total_q].
+``attn_splitkv_workspace_bytes``, ``attn_pack_gqa_heuristic``,
+``attn_num_splits_heuristic``
+    Sizing helpers of attn_fwd_ex (pure host functions).
 ``attn_last_error()``
     Message of the last failed call on this thread.
 
 Convenience wrappers that allocate the outputs with torch: ``attention``,
-``attention_backward`` and ``fp8_prepare``/``attention_fp8``.
+``attention_ex``, ``attention_backward`` and ``fp8_prepare``/``attention_fp8``.
 """
 from __future__ import annotations
 
@@ -35,8 +44,10 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd",
-    "attn_last_error", "attention", "attention_backward", "fp8_prepare", "attention_fp8", "EXPORTED_SYMBOLS",
+    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_fwd_ex",
+    "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
+    "attn_last_error", "attention", "attention_ex", "attention_backward", "fp8_prepare", "attention_fp8",
+    "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +56,9 @@ _lib = None
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 DTYPE_BF16, DTYPE_F16 = 0, 1
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_last_error", "attn_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_fwd_ex",
+                    "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
+                    "attn_last_error", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -72,6 +85,15 @@ def load():
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_bwd.restype = i
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, f, i, i, i, vp,
+                                ctypes.c_int64, vp]
+    lib.attn_fwd_ex.restype = i
+    lib.attn_splitkv_workspace_bytes.argtypes = [i, i, i, i]
+    lib.attn_splitkv_workspace_bytes.restype = ctypes.c_int64
+    lib.attn_pack_gqa_heuristic.argtypes = [i, i, i]
+    lib.attn_pack_gqa_heuristic.restype = i
+    lib.attn_num_splits_heuristic.argtypes = [i, i, i, i, i, i, i, i]
+    lib.attn_num_splits_heuristic.restype = i
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -137,6 +159,92 @@ def attn_fwd(q, k, v, o, lse, causal=False, alpha=None, stream=None):
     _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)),
                         _default_alpha(d, alpha), dt, _stream_handle(stream)))
     return o, lse
+
+
+def attn_splitkv_workspace_bytes(num_splits, total_q, Hq, d):
+    return int(load().attn_splitkv_workspace_bytes(int(num_splits), int(total_q), int(Hq), int(d)))
+
+
+def attn_pack_gqa_heuristic(Hq, Hkv, Nq):
+    return int(load().attn_pack_gqa_heuristic(int(Hq), int(Hkv), int(Nq)))
+
+
+def attn_num_splits_heuristic(B, Hq, Hkv, Nq, Nk, d, pack_gqa=-1, num_cus=None):
+    if num_cus is None:
+        num_cus = _torch().cuda.get_device_properties(0).multi_processor_count
+    return int(load().attn_num_splits_heuristic(int(B), int(Hq), int(Hkv), int(Nq), int(Nk), int(d),
+                                                int(pack_gqa), int(num_cus)))
+
+
+def _ex_shapes(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
+    """(B, Hq, Hkv, Nq, Nk, d, total_q, total_k, lse shape) of an attn_fwd_ex call."""
+    if cu_seqlens_q is None:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("dense inputs: q must be [B, Nq, Hq, d] and k [B, Nk, Hkv, d]")
+        B, Nq, Hq, d = q.shape
+        Nk, Hkv = k.shape[1], k.shape[2]
+        return B, Hq, Hkv, Nq, Nk, d, B * Nq, B * Nk, (B, Hq, Nq)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed inputs: q must be [total_q, Hq, d] and k [total_k, Hkv, d]")
+    if max_seqlen_q is None or max_seqlen_k is None:
+        raise ValueError("packed inputs need max_seqlen_q and max_seqlen_k")
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    return B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), d, total_q, total_k, (Hq, total_q)
+
+
+def attn_fwd_ex(q, k, v, o, lse, causal=False, alpha=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, workspace=None, stream=None):
+    """Forward with grouped heads, N_q != N_k, packed batches and split-KV."""
+    torch = _torch()
+    lib = load()
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    B, Hq, Hkv, Nq, Nk, d, total_q, total_k, lse_shape = _ex_shapes(q, k, cu_seqlens_q, cu_seqlens_k,
+                                                                    max_seqlen_q, max_seqlen_k)
+    _require(q, "q", q.dtype, q.shape, q.device)
+    _require(o, "o", q.dtype, q.shape, q.device)
+    _require(k, "k", q.dtype, k.shape, q.device)
+    _require(v, "v", q.dtype, k.shape, q.device)
+    _require(lse, "lse", torch.float32, lse_shape, q.device)
+    cu_q = cu_k = ctypes.c_void_p(0)
+    if cu_seqlens_q is not None:
+        _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,), q.device)
+        _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, (B + 1,), q.device)
+        cu_q, cu_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    ws, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        if workspace.dtype != torch.float32 or workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous float32 tensor on the device of q")
+        ws, ws_bytes = _ptr(workspace), workspace.numel() * 4
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    _check(lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, cu_q, cu_k,
+                           total_q, total_k, int(bool(causal)), _default_alpha(d, alpha), dt, int(pack_gqa),
+                           int(num_splits), ws, ctypes.c_int64(ws_bytes), _stream_handle(stream)))
+    return o, lse
+
+
+def attention_ex(q, k, v, causal=False, alpha=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                 max_seqlen_k=None, pack_gqa=-1, num_splits=None, stream=None):
+    """Allocate O, LSE and the split-KV workspace with torch and run attn_fwd_ex.
+
+    ``num_splits=None`` takes attn_num_splits_heuristic for this device.
+    """
+    torch = _torch()
+    B, Hq, Hkv, Nq, Nk, d, total_q, _, lse_shape = _ex_shapes(q, k, cu_seqlens_q, cu_seqlens_k,
+                                                              max_seqlen_q, max_seqlen_k)
+    if num_splits is None:
+        num_splits = attn_num_splits_heuristic(B, Hq, Hkv, Nq, Nk, d, pack_gqa,
+                                               torch.cuda.get_device_properties(q.device).multi_processor_count)
+    o = torch.empty_like(q)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    nbytes = attn_splitkv_workspace_bytes(num_splits, total_q, Hq, d)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device) if nbytes else None
+    return attn_fwd_ex(q, k, v, o, lse, causal, alpha, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                       pack_gqa, num_splits, ws, stream)
 
 
 def attn_fp8_prepare(x, x8, descale, block_rows=128, hadamard=False, seed=0, stream=None):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fp8.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fp8.hip", "attn_bwd.hip", "attn_decode.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",

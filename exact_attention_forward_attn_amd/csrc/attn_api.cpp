@@ -50,9 +50,9 @@ int check_shape(int B, int H, int N, int d, int elem_bytes) {
   if (d != 64 && d != 128 && d != 256)
     return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d is not supported (64, 128 or 256)", d);
   if (B == 0 || H == 0 || N == 0) return 1;
-  // the kernels address one head with 32-bit byte offsets and index rows
-  // and LSE entries with 32-bit integers
-  const int64_t head_span = (int64_t)(N - 1) * H * d * elem_bytes + (int64_t)d * elem_bytes;
+  // the kernels address one head with 32-bit byte offsets (up to a tile
+  // past its last row) and index rows and LSE entries with 32-bit integers
+  const int64_t head_span = ((int64_t)N + 128) * H * d * elem_bytes;
   if (head_span >= (int64_t(1) << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "N*H*d too large for one batch entry (%lld bytes >= 2^31)",
                 (long long)head_span);
@@ -116,7 +116,146 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.causal = causal;
   a.dtype = dtype;
   a.scale_log2 = scale_log2(alpha);
+  a.Hkv = H; a.Nk = N;
+  a.total_q = a.total_k = B * N;
+  a.nsplit = 1;
   return hip_status(attn::launch_fwd_16(a, stream), "attn_fwd launch");
+}
+
+int64_t attn_splitkv_workspace_bytes(int num_splits, int total_q, int Hq, int d) {
+  if (num_splits <= 1 || total_q <= 0 || Hq <= 0 || d <= 0) return 0;
+  return (int64_t)num_splits * total_q * Hq * (d + 1) * 4;
+}
+
+int attn_pack_gqa_heuristic(int Hq, int Hkv, int Nq) {
+  if (Hkv <= 0 || Hq <= Hkv || Hq % Hkv != 0 || Nq <= 0) return 0;
+  const int64_t g = Hq / Hkv;
+  // pack when it takes fewer 128-row query tiles
+  return ((int64_t)Nq * g + 127) / 128 < g * (((int64_t)Nq + 127) / 128) ? 1 : 0;
+}
+
+int attn_num_splits_heuristic(int B, int Hq, int Hkv, int Nq, int Nk, int d, int pack_gqa, int num_cus) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Nq <= 0 || Nk <= 0 || num_cus <= 0) return 1;
+  const int64_t g = Hq / Hkv;
+  int64_t blocks, target, min_keys;
+  if (attn::uses_decode_kernel(Nq, Hq, Hkv, d)) {
+    // decode kernel: one workgroup per (sequence, KV head, range); about one
+    // per compute unit, each range long enough to amortise its start-up
+    blocks = (int64_t)B * Hkv;
+    target = num_cus;
+    min_keys = 512;
+  } else {
+    const bool pack = pack_gqa < 0 ? attn_pack_gqa_heuristic(Hq, Hkv, Nq) != 0 : (pack_gqa != 0 && g > 1);
+    const int64_t rows = pack ? (int64_t)Nq * g : Nq;
+    blocks = (rows + 127) / 128 * B * (pack ? Hkv : Hq);
+    target = (int64_t)num_cus * (d == 256 ? 1 : 2);  // resident workgroups
+    min_keys = 256;
+  }
+  if (blocks >= target) return 1;
+  int64_t s = (target + blocks - 1) / blocks;
+  const int64_t by_keys = ((int64_t)Nk + min_keys - 1) / min_keys;
+  if (s > by_keys) s = by_keys;
+  if (s > 128) s = 128;
+  return s < 1 ? 1 : (int)s;
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                int Nq, int Nk, int d, const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q,
+                int total_k, int causal, float alpha, int dtype, int pack_gqa, int num_splits,
+                float* workspace, int64_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "B, Hq, Hkv, Nq, Nk must be >= 0 (got %d, %d, %d, %d, %d)", B, Hq, Hkv,
+                Nq, Nk);
+  if (d != 64 && d != 128 && d != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d is not supported (64, 128 or 256)", d);
+  if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0))
+    return fail(ATTN_ERR_INVALID_ARG, "Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!std::isfinite(alpha) || alpha < 0.f)
+    return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
+  if (pack_gqa < -1 || pack_gqa > 1) return fail(ATTN_ERR_INVALID_ARG, "pack_gqa must be -1, 0 or 1");
+  if (num_splits < 1) return fail(ATTN_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", num_splits);
+  const bool varlen = cu_seqlens_q != nullptr || cu_seqlens_k != nullptr;
+  if (varlen && (!cu_seqlens_q || !cu_seqlens_k))
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must both be given or both be null");
+  if (varlen && (total_q < 0 || total_k < 0))
+    return fail(ATTN_ERR_INVALID_ARG, "total_q, total_k must be >= 0 (got %d, %d)", total_q, total_k);
+  if (!varlen) {
+    if ((int64_t)B * Nq >= (int64_t(1) << 31) || (int64_t)B * Nk >= (int64_t(1) << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, "B*Nq or B*Nk too large (>= 2^31)");
+    total_q = B * Nq;
+    total_k = B * Nk;
+  }
+  if (B == 0 || Hq == 0 || Nq == 0 || total_q == 0) return ok();
+  // kernels address one sequence of one head with 32-bit byte offsets (up to
+  // a tile past its end) and index rows, LSE entries and tiles with 32-bit
+  // integers
+  if (((int64_t)Nq + 128) * Hq * d * 2 >= (int64_t(1) << 31) || ((int64_t)Nk + 128) * Hkv * d * 2 >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "sequence too long for the number of heads (N*H*d*2 near 2^31)");
+  if ((int64_t)total_q * Hq >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "total_q*Hq too large (>= 2^31)");
+  const int g = Hq / Hkv;
+  const int pack = pack_gqa < 0 ? attn_pack_gqa_heuristic(Hq, Hkv, Nq) : (pack_gqa && g > 1 ? 1 : 0);
+  // effective key ranges: a multiple of 64 keys each, none empty
+  int split_len = 0, nsplit = 1;
+  if (num_splits > 1 && Nk > 0) {
+    const int64_t per = ((int64_t)Nk + num_splits - 1) / num_splits;
+    split_len = (int)((per + 63) / 64 * 64);
+    nsplit = (int)(((int64_t)Nk + split_len - 1) / split_len);
+  }
+  const int64_t rows = pack ? (int64_t)Nq * g : Nq;
+  const int64_t grid = (rows + 127) / 128 * B * (pack ? Hkv : Hq) * nsplit;
+  if (grid >= (int64_t(1) << 31)) return fail(ATTN_ERR_UNSUPPORTED, "too many workgroups (>= 2^31)");
+  const void* ptrs[5] = {q, k, v, o, lse};
+  const char* names[5] = {"q", "k", "v", "o", "lse"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  if (varlen && ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens are not 4-byte aligned");
+  const int64_t qb = (int64_t)total_q * Hq * d * 2, kb = (int64_t)total_k * Hkv * d * 2;
+  const int64_t lb = (int64_t)total_q * Hq * 4;
+  const int64_t ws_need = nsplit > 1 ? attn_splitkv_workspace_bytes(nsplit, total_q, Hq, d) : 0;
+  const void* in[3] = {q, k, v};
+  const int64_t in_b[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, qb, in[i], in_b[i])) return fail(ATTN_ERR_INVALID_ARG, "o overlaps %s", names[i]);
+    if (overlaps(lse, lb, in[i], in_b[i])) return fail(ATTN_ERR_INVALID_ARG, "lse overlaps %s", names[i]);
+  }
+  if (overlaps(o, qb, lse, lb)) return fail(ATTN_ERR_INVALID_ARG, "o overlaps lse");
+  if (ws_need > 0) {
+    if (!workspace) return fail(ATTN_ERR_INVALID_ARG, "workspace is null but %d key ranges need %lld bytes", nsplit,
+                                (long long)ws_need);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < ws_need)
+      return fail(ATTN_ERR_INVALID_ARG, "workspace has %lld bytes, %d key ranges need %lld", (long long)workspace_bytes,
+                  nsplit, (long long)ws_need);
+    const void* all[5] = {q, k, v, o, lse};
+    const int64_t all_b[5] = {qb, kb, kb, qb, lb};
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(workspace, ws_need, all[i], all_b[i]))
+        return fail(ATTN_ERR_INVALID_ARG, "workspace overlaps %s", names[i]);
+  }
+  attn::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.H = Hq; a.N = Nq; a.d = d;
+  a.causal = causal;
+  a.dtype = dtype;
+  a.scale_log2 = scale_log2(alpha);
+  a.Hkv = Hkv; a.Nk = Nk;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.total_q = total_q; a.total_k = total_k;
+  a.pack = pack;
+  a.nsplit = nsplit;
+  a.split_len = split_len;
+  if (nsplit > 1) {
+    a.opart = workspace;
+    a.lpart = workspace + (int64_t)nsplit * total_q * Hq * d;
+  }
+  return hip_status(attn::launch_fwd_16(a, stream), "attn_fwd_ex launch");
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

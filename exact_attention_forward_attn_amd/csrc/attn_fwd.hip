@@ -63,9 +63,19 @@ struct KernelArgs {
   const void* v;
   void* o;
   float* lse;
-  int B, H, N;
-  int n_mblk;     // ceil(N / BM)
-  float c;        // alpha * log2(e)
+  float* opart;       // split partials (null unless nsplit > 1)
+  float* lpart;
+  const int* cu_q;    // packed batches: row offsets, else null
+  const int* cu_k;
+  int Hq, Hkv, g;     // query heads, key/value heads, g = Hq / Hkv
+  int Nq, Nk;         // rows per batch entry (maxima for packed batches)
+  int total_q, total_k;
+  int hu;             // head units per batch entry: Hkv if packed, else Hq
+  int pack;
+  int n_mblk;         // query blocks per (batch entry, head unit)
+  int nunit;          // B * hu
+  int nsplit, split_len;
+  float c;            // alpha * log2(e)
 };
 
 // Waves per SIMD each kernel is compiled for (its register budget).
@@ -122,30 +132,63 @@ void fwd_kernel(KernelArgs a) {
   const int l32 = lane & 31;
 
   // ---- work decomposition -------------------------------------------------
-  const int BH = a.B * a.H;
-  int mblk, bh;
-  decode_block(blockIdx.x, a.n_mblk, BH, CAUSAL, mblk, bh);
-  const int b = bh / a.H;
-  const int hh = bh % a.H;
-  const int N = a.N;
+  // workgroup -> (query block, head unit, key range). A head unit is one
+  // query head, or with packing one key/value head and its g query heads,
+  // whose rows interleave: tile row r is query r / g of head r % g of the
+  // group (the KV head of query head h is floor(h / g), "FlashAttention-3 on
+  // Hopper", section 5.6.1).
+  int mblk, rest;
+  decode_block(blockIdx.x, a.n_mblk, a.nunit * a.nsplit, CAUSAL, mblk, rest);
+  const int unit = rest / a.nsplit;
+  const int split = rest - unit * a.nsplit;
+  const int b = unit / a.hu;
+  const int hu = unit - b * a.hu;
+  const int grp = a.g;
+  const bool pack = a.pack != 0;
+  // rows of this batch entry in q/o and k/v; offsets of packed batches are
+  // clamped into the tensors, so malformed offsets never address outside
+  int q_row0, len_q, k_row0, len_k;
+  if (a.cu_q) {
+    q_row0 = min(max(a.cu_q[b], 0), a.total_q);
+    len_q = min(min(max(a.cu_q[b + 1], q_row0), a.total_q) - q_row0, a.Nq);
+    k_row0 = min(max(a.cu_k[b], 0), a.total_k);
+    len_k = min(min(max(a.cu_k[b + 1], k_row0), a.total_k) - k_row0, a.Nk);
+  } else {
+    q_row0 = b * a.Nq; len_q = a.Nq;
+    k_row0 = b * a.Nk; len_k = a.Nk;
+  }
+  const int rows = pack ? len_q * grp : len_q;  // tile rows of this unit
   const int q0 = mblk * BM;
-  const int qw = q0 + wave * 32;              // first query row of this wave
-  const int qi = qw + l32;                    // this lane's query row
-  const uint32_t RS = (uint32_t)a.H * D * 2;  // bytes between consecutive rows
-  const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;  // elements
-  const uint32_t span = (uint32_t)(N - 1) * RS + D * 2;       // valid bytes of this head
-
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + head_off, span);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + head_off, span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + head_off, span);
+  if (q0 >= rows) return;  // past a short sequence (uniform over the workgroup)
+  const int qw = q0 + wave * 32;              // first tile row of this wave
+  const int qi = qw + l32;                    // this lane's tile row
+  const int n_i = pack ? qi / grp : qi;       // its query index
+  const int hq_i = pack ? hu * grp + (qi - n_i * grp) : hu;  // its query head
+  const int hk = pack ? hu : hu / grp;
+  const int off = len_k - len_q;              // causal offset (bottom-right)
+  const uint32_t RSQ = (uint32_t)a.Hq * D * 2;   // bytes between query rows
+  const uint32_t RSK = (uint32_t)a.Hkv * D * 2;  // bytes between key rows
+  const int hq0 = pack ? hu * grp : hu;       // first query head of the unit
+  const int64_t q_off = ((int64_t)q_row0 * a.Hq + hq0) * D;  // elements
+  const int64_t k_off = ((int64_t)k_row0 * a.Hkv + hk) * D;
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc((const T*)a.q + q_off, (uint32_t)(len_q - 1) * RSQ + (uint32_t)(pack ? grp : 1) * D * 2);
+  const uint32_t kspan = len_k > 0 ? (uint32_t)(len_k - 1) * RSK + D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + k_off, kspan);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + k_off, kspan);
 
   // ---- Q^T operands (B operand of S^T = K Q^T), resident in VGPRs ----------
+  // (rows past the unit's end read as zero through the buffer range check)
+  const uint32_t qofs = (uint32_t)n_i * RSQ + (uint32_t)(hq_i - hq0) * D * 2;
   v8 qreg[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
-    u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)qi * RS + (16 * kc + 8 * h32) * 2, 0, 0);
+    u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(rq, qofs + (16 * kc + 8 * h32) * 2, 0, 0);
     qreg[kc] = __builtin_bit_cast(v8, raw);
   }
+
+  // last key of this lane's row, less the lane's key offset in a tile
+  const int diag = n_i + off - 4 * h32;
 
   // ---- per-lane LDS offsets -------------------------------------------------
   // global -> LDS copy: segment seg = wave + 4t, lane i covers row seg*RPS +
@@ -159,12 +202,12 @@ void fwd_kernel(KernelArgs a) {
   for (int t = 0; t < KGP; ++t) {
     const int r = (wave + 4 * t) * G::RPS + lane / G::CPR;
     const int pc = lane % G::CPR;
-    kg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * 4 * G::RPS * RS;
+    kg[t] = (uint32_t)r * RSK + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * 4 * G::RPS * RSK;
   }
   {
     const int r = wave * G::RPS + lane / G::CPR;
     const int pc = lane % G::CPR;
-    vg0 = (uint32_t)r * RS + (uint32_t)((pc ^ swz_v<D>(r)) << 4);
+    vg0 = (uint32_t)r * RSK + (uint32_t)((pc ^ swz_v<D>(r)) << 4);
   }
   // K operand reads: row kb*32 + l32, logical chunk 2kc + h32
   int kofs[KCL];
@@ -199,14 +242,24 @@ void fwd_kernel(KernelArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
-  const int nt = (kv_end + BN - 1) / BN;
-  // Processing order i = 0 .. nt-1 visits KV tile j = nt-1-i (descending).
-  // The tiles this wave must mask (tail past N, keys right of its diagonal)
-  // form a prefix of that order: tile j is masked iff j >= jm.
-  int jm = N >= BN ? (N - BN) / BN + 1 : 0;
+  // Keys of this workgroup: its key range [kb0, kb1), cut short (causal) at
+  // the last key its last query sees. Query n sees key j iff
+  // j <= n + (len_k - len_q) ("FlashAttention-3 on Hopper", section 4.7).
+  const int kb0 = split * a.split_len;
+  const int kb1 = min(len_k, kb0 + a.split_len);
+  int kv_end = kb1;
   if (CAUSAL) {
-    const int x = qw - BN + 1;
+    const int n_last = min(len_q - 1, pack ? (q0 + BM - 1) / grp : q0 + BM - 1);
+    kv_end = min(kv_end, n_last + off + 1);
+  }
+  const int nt = kv_end > kb0 ? (kv_end - kb0 + BN - 1) / BN : 0;
+  // Processing order i = 0 .. nt-1 visits KV tile j = nt-1-i (descending;
+  // tile j starts at key kb0 + j*BN). The tiles this wave must mask (keys at
+  // or past kb1, keys right of its diagonal) form a prefix of that order:
+  // tile j is masked iff j >= jm.
+  int jm = kb1 - kb0 >= BN ? (kb1 - kb0 - BN) / BN + 1 : 0;
+  if (CAUSAL) {
+    const int x = (pack ? qw / grp : qw) + off - kb0 - BN + 1;
     jm = min(jm, x >= 0 ? x / BN + 1 : 0);
   }
   const int n_masked = max(0, nt - jm);
@@ -219,12 +272,12 @@ void fwd_kernel(KernelArgs a) {
   // the VGPR offset: the buffer range check, which zero-fills rows past N,
   // does not cover the scalar offset.)
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) ATTN_INLINE {
-    const uint32_t base = (uint32_t)((nt - 1 - i) * BN) * RS;
+    const uint32_t base = (uint32_t)(kb0 + (nt - 1 - i) * BN) * RSK;
     const uint32_t g0 = is_k ? kg[0] : vg0;
     const uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
 #pragma unroll
     for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
-      const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * 4 * G::RPS * RS);
+      const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * 4 * G::RPS * RSK);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + 4 * t) * 1024), 16, voff, 0, 0, 0);
     }
   };
@@ -252,14 +305,14 @@ void fwd_kernel(KernelArgs a) {
     }
   };
 
-  // Scores of keys past N or right of the diagonal become -inf (only the
-  // tiles of the masked prefix call this). kv0: first key of the tile.
+  // Scores of keys at or past kb1 or right of the diagonal become -inf (only
+  // the tiles of the masked prefix call this). kv0: first key of the tile.
   auto apply_mask = [&](auto sb_tag, int kv0) ATTN_INLINE {
     constexpr int SB = decltype(sb_tag)::value;
     // key offset within the tile = 4*h32 + o with o a compile-time constant,
     // so compare o against per-lane thresholds (no per-element index vectors)
-    const int tn = N - kv0 - 4 * h32;          // o >= tn: key at or past N
-    const int tc = qi - kv0 - 4 * h32;         // o > tc: key right of the diagonal
+    const int tn = kb1 - kv0 - 4 * h32;        // o >= tn: key at or past kb1
+    const int tc = diag - kv0;                 // o > tc: key right of the diagonal
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -433,6 +486,11 @@ void fwd_kernel(KernelArgs a) {
     if constexpr (DO_SM) finish_tile(Int<SN>{});
   };
 
+  // A workgroup with no visible key (causal with N_q > N_k, an empty key
+  // range or sequence) skips to the epilogue, which then writes O = 0 and
+  // LSE = -inf. nt is uniform over the workgroup, so every barrier inside is
+  // reached by all of its waves or by none.
+  if (nt > 0) {
   // prologue: K_0, K_1, V_0; S_0, S_1; P_0; then K_2 into K_0's slot
   issue(rk, true, kbuf0, 0);
   if (nt > 1) issue(rk, true, kbuf1, 1);
@@ -443,8 +501,8 @@ void fwd_kernel(KernelArgs a) {
   if (nt > 1) qk(Int<1>{}, kbuf1);
   barrier();  // every wave has read K_0
   if (nt > 2) issue(rk, true, kbuf0, 2);
-  if (n_masked > 0) apply_mask(Int<0>{}, (nt - 1) * BN);
-  if (n_masked > 1) apply_mask(Int<1>{}, (nt - 2) * BN);
+  if (n_masked > 0) apply_mask(Int<0>{}, kb0 + (nt - 1) * BN);
+  if (n_masked > 1) apply_mask(Int<1>{}, kb0 + (nt - 2) * BN);
   {
     constexpr Sched S0{16};
     For<0, S0.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<16>{}, TrueT{}); });
@@ -461,7 +519,7 @@ void fwd_kernel(KernelArgs a) {
     if (i + 1 < nt) issue(rv, false, vslot(Int<J + 1>{}), i + 1);
     if (i + 3 < nt) issue(rk, true, kslot(Int<J + 1>{}), i + 3);
     block(j_tag, qk_tag, sm_tag);
-    if (decltype(qk_tag)::value && i + 2 < n_masked) apply_mask(Int<J>{}, (nt - 3 - i) * BN);
+    if (decltype(qk_tag)::value && i + 2 < n_masked) apply_mask(Int<J>{}, kb0 + (nt - 3 - i) * BN);
   };
   // unrolled by two (the trip count is uniform over the workgroup), which
   // makes every slot and buffer index a compile-time constant
@@ -481,31 +539,128 @@ void fwd_kernel(KernelArgs a) {
   } else {
     iteration(i, Int<0>{}, FalseT{}, FalseT{});
   }
+  }  // nt > 0
 
   // ---- finalize and epilogue ------------------------------------------------
   const float lt = lacc[0];
   const float ll = halves_sum(l_lse);
   const bool ok = lt > 0.f;  // false for 0 and NaN
   const float inv = ok ? 1.0f / lt : 0.f;
-  if (qi < N) {
-    if (h32 == 0) {
-      const float lse = ok ? (m_run * c + __builtin_amdgcn_logf(ll)) * kLn2 : -__builtin_inff();
-      a.lse[(int64_t)bh * N + qi] = lse;
-    }
-    T* orow = (T*)a.o + head_off + (int64_t)qi * a.H * D;
+  // The row indices are recomputed from a fresh read of the lane id (asm
+  // volatile, so the compiler cannot reuse the prologue's values), which
+  // frees their registers during the loop.
+  int lane_e;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int qi_e = qw + (lane_e & 31);
+  const int ne = pack ? qi_e / grp : qi_e;
+  const int hq_e = pack ? hu * grp + (qi_e - ne * grp) : hu;
+  if (qi_e < rows) {
+    const float lse = ok ? (m_run * c + __builtin_amdgcn_logf(ll)) * kLn2 : -__builtin_inff();
+    const int64_t qrow = (int64_t)q_row0 + ne;  // row in q / o
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    if (a.nsplit > 1) {
+      // normalised state of this key range, float32 (merged by the combine
+      // kernel)
+      const int64_t pr = ((int64_t)split * a.total_q + qrow) * a.Hq + hq_e;
+      if (h32 == 0) a.lpart[pr] = lse;
+      float* orow = a.opart + pr * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        typedef T t4 __attribute__((ext_vector_type(4)));
-        float __attribute__((ext_vector_type(4))) f;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f4 f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * g + e] * inv;
-        t4 ov = __builtin_convertvector(f, t4);
-        *(u32x2*)(orow + db * 32 + 8 * g + 4 * h32) = __builtin_bit_cast(u32x2, ov);
+          for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * q4 + e] * inv;
+          *(f4*)(orow + db * 32 + 8 * q4 + 4 * h32) = f;
+        }
+    } else {
+      if (h32 == 0) {
+        // LSE is [B, Hq, Nq] for dense inputs and [Hq, total_q] for packed
+        // batches
+        const int64_t li = a.cu_q ? (int64_t)hq_e * a.total_q + qrow : ((int64_t)b * a.Hq + hq_e) * a.Nq + ne;
+        a.lse[li] = lse;
       }
+      T* orow = (T*)a.o + (qrow * a.Hq + hq_e) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          typedef T t4 __attribute__((ext_vector_type(4)));
+          f4 f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * q4 + e] * inv;
+          t4 ov = __builtin_convertvector(f, t4);
+          *(u32x2*)(orow + db * 32 + 8 * q4 + 4 * h32) = __builtin_bit_cast(u32x2, ov);
+        }
+    }
   }
 #endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---- split-KV combine -------------------------------------------------------
+// Merges the normalised states (O_s, LSE_s) that the key ranges of one
+// (query row, query head) left in the workspace: LSE = ln sum_s e^(LSE_s),
+// O = sum_s e^(LSE_s - LSE) O_s. This is the block-combine rule of
+// "FlashAttention-3 on Hopper", section 3.2.1, in the units O = O~ / l and
+// LSE = m + ln l; the pages name a separate combine kernel for split-KV
+// (chapter 10). One wave per (row, head); lane l owns dims D/64 * l ...
+struct CombineArgs {
+  const float* opart;  // [nsplit, npairs, D]
+  const float* lpart;  // [nsplit, npairs]
+  void* o;             // [total_q, Hq, D] (pair = row * Hq + head)
+  float* lse;
+  int npairs;          // total_q * Hq
+  int nsplit;
+  int Hq, Nq, total_q;
+  int varlen;          // LSE layout: [Hq, total_q] if set, else [B, Hq, Nq]
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  constexpr int PER = D / 64;
+  typedef float fv __attribute__((ext_vector_type(PER)));
+  typedef T tv __attribute__((ext_vector_type(PER)));
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.npairs) return;
+  float mx = -__builtin_inff();
+  for (int s = lane; s < a.nsplit; s += 64) mx = __builtin_fmaxf(mx, a.lpart[(int64_t)s * a.npairs + pair]);
+  mx = wave_max(mx);
+  const bool ok = mx > -__builtin_inff();  // some range saw a key
+  float sum = 0.f;
+  if (ok)
+    for (int s = lane; s < a.nsplit; s += 64)
+      sum += exp2_fast((a.lpart[(int64_t)s * a.npairs + pair] - mx) * kLog2e);  // -inf -> 0
+  sum = wave_sum(sum);  // >= 1: the maximal range contributes e^0
+  const float lse = ok ? mx + __builtin_amdgcn_logf(sum) * kLn2 : -__builtin_inff();
+  fv acc = {};
+  if (ok) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const int64_t sp = (int64_t)s * a.npairs + pair;
+      const float w = exp2_fast((a.lpart[sp] - lse) * kLog2e);
+      if (w == 0.f) continue;  // empty range (uniform over the wave)
+      acc += w * *(const fv*)(a.opart + sp * D + PER * lane);
+    }
+  }
+  *(tv*)((T*)a.o + (int64_t)pair * D + PER * lane) = __builtin_convertvector(acc, tv);
+  if (lane == 0) {
+    const int row = pair / a.Hq, h = pair - row * a.Hq;
+    const int64_t li = a.varlen ? (int64_t)h * a.total_q + row
+                                : ((int64_t)(row / a.Nq) * a.Hq + h) * a.Nq + row % a.Nq;
+    a.lse[li] = lse;
+  }
 }
 
 template <int D, int KB, bool CAUSAL, typename T>
@@ -513,11 +668,33 @@ int launch(const FwdArgs& f, hipStream_t st) {
   constexpr int BM = 128;
   KernelArgs a;
   a.q = f.q; a.k = f.k; a.v = f.v; a.o = f.o; a.lse = f.lse;
-  a.B = f.B; a.H = f.H; a.N = f.N;
-  a.n_mblk = (f.N + BM - 1) / BM;
+  a.opart = f.opart; a.lpart = f.lpart;
+  a.cu_q = f.cu_q; a.cu_k = f.cu_k;
+  a.Hq = f.H; a.Hkv = f.Hkv; a.g = f.H / f.Hkv;
+  a.Nq = f.N; a.Nk = f.Nk;
+  a.total_q = f.total_q; a.total_k = f.total_k;
+  a.pack = (f.pack && a.g > 1) ? 1 : 0;
+  a.hu = a.pack ? f.Hkv : f.H;
+  const int rows = a.pack ? f.N * a.g : f.N;
+  a.n_mblk = (rows + BM - 1) / BM;
+  a.nunit = f.B * a.hu;
+  a.nsplit = f.nsplit > 1 ? f.nsplit : 1;
+  a.split_len = f.nsplit > 1 ? f.split_len : 0x7fffffff;
   a.c = f.scale_log2;
-  const int grid = a.n_mblk * f.B * f.H;
+  const int grid = a.n_mblk * a.nunit * a.nsplit;
   hipLaunchKernelGGL((fwd_kernel<D, KB, CAUSAL, T>), dim3(grid), dim3(256), 0, st, a);
+  return (int)hipGetLastError();
+}
+
+template <int D, typename T>
+int launch_combine(const FwdArgs& f, hipStream_t st) {
+  CombineArgs cb;
+  cb.opart = f.opart; cb.lpart = f.lpart; cb.o = f.o; cb.lse = f.lse;
+  cb.npairs = f.total_q * f.H;
+  cb.nsplit = f.nsplit;
+  cb.Hq = f.H; cb.Nq = f.N; cb.total_q = f.total_q;
+  cb.varlen = f.cu_q != nullptr;
+  hipLaunchKernelGGL((combine_kernel<D, T>), dim3((cb.npairs + 3) / 4), dim3(256), 0, st, cb);
   return (int)hipGetLastError();
 }
 
@@ -539,20 +716,30 @@ int dispatch_d(const FwdArgs& f, hipStream_t st) {
 }
 
 template <typename T>
-int dispatch(const FwdArgs& f, hipStream_t st) {
+int dispatch(const FwdArgs& f, hipStream_t st, bool combine) {
   switch (f.d) {
-    case 64: return dispatch_d<64, T>(f, st);
-    case 128: return dispatch_d<128, T>(f, st);
-    case 256: return dispatch_d<256, T>(f, st);
+    case 64: return combine ? launch_combine<64, T>(f, st) : dispatch_d<64, T>(f, st);
+    case 128: return combine ? launch_combine<128, T>(f, st) : dispatch_d<128, T>(f, st);
+    case 256: return combine ? launch_combine<256, T>(f, st) : dispatch_d<256, T>(f, st);
   }
   return (int)hipErrorInvalidValue;
 }
 
 }  // namespace fwd16
 
+// Sequences with at most kDecodeRows query rows per key/value head (query
+// rows times g) and d <= 128 go to the decode kernel, the others to the
+// tiled kernel; with several key ranges the combine kernel follows either.
 int launch_fwd_16(const FwdArgs& f, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  return f.dtype == 0 ? fwd16::dispatch<__bf16>(f, st) : fwd16::dispatch<_Float16>(f, st);
+  const bool bf = f.dtype == 0;
+  int err;
+  if (uses_decode_kernel(f.N, f.H, f.Hkv, f.d))
+    err = launch_decode_16(f, stream);
+  else
+    err = bf ? fwd16::dispatch<__bf16>(f, st, false) : fwd16::dispatch<_Float16>(f, st, false);
+  if (err || f.nsplit <= 1) return err;
+  return bf ? fwd16::dispatch<__bf16>(f, st, true) : fwd16::dispatch<_Float16>(f, st, true);
 }
 
 const char* hip_error_name(int err) { return hipGetErrorString((hipError_t)err); }

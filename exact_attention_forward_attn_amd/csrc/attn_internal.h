@@ -16,11 +16,25 @@ struct FwdArgs {
   const float* dq;  // FP8 descales (null for 16-bit inputs)
   const float* dk;
   const float* dv;
-  int B, H, N, d;
+  int B, H, N, d;  // H: query heads; N: query rows per batch entry (the
+                   // maximum over the sequences for packed batches)
   int causal;
   int dtype;       // 0 bf16, 1 f16 (16-bit path)
   int block_rows;  // FP8: 128 or 0 (per tensor)
   float scale_log2;  // alpha * log2(e), clamped to >= 1e-30
+  // 16-bit path only (the FP8 path requires Hkv = H, Nk = N, no packing,
+  // one split):
+  int Hkv;           // key/value heads (H % Hkv == 0)
+  int Nk;            // key rows per batch entry (maximum for packed batches)
+  const int* cu_q;   // packed batches: B + 1 row offsets (device), else null
+  const int* cu_k;
+  int total_q;       // rows of q and o (B * N for dense inputs)
+  int total_k;       // rows of k and v
+  int pack;          // query heads of one key/value head share a tile
+  int nsplit;        // key ranges (1: no split)
+  int split_len;     // keys per range, a multiple of 64
+  float* opart;      // nsplit > 1: [nsplit, total_q, H, d] float32 partial O
+  float* lpart;      //             [nsplit, total_q, H] float32 partial LSE
 };
 
 struct BwdArgs {
@@ -51,8 +65,16 @@ struct PrepArgs {
   uint64_t seed;
 };
 
+// Query rows per key/value head (N_q * H / Hkv) up to which the 16-bit
+// forward runs the decode kernel (d = 64 and 128).
+constexpr int kDecodeRows = 16;
+inline bool uses_decode_kernel(int Nq, int Hq, int Hkv, int d) {
+  return d <= 128 && (int64_t)Nq * (Hq / Hkv) <= kDecodeRows;
+}
+
 // Each returns 0 on success or a hipError_t value.
 int launch_fwd_16(const FwdArgs& a, void* stream);
+int launch_decode_16(const FwdArgs& a, void* stream);
 int launch_fwd_fp8(const FwdArgs& a, void* stream);
 int launch_fp8_prepare(const PrepArgs& a, void* stream);
 int launch_bwd_16(const BwdArgs& a, void* stream);

@@ -158,6 +158,78 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, int causal, float alpha,
              int dtype, void* stream);
 
+/*
+ * attn_fwd_ex -- the 16-bit forward of attn_fwd, generalised for serving:
+ * grouped / multi-query heads, N_q != N_k, packed variable-length batches,
+ * and split-KV (Flash-Decoding) with a combine kernel.
+ *
+ *   Heads    Hq query heads over Hkv key/value heads (Hq % Hkv == 0); query
+ *            head h reads key/value head floor(h / (Hq / Hkv))
+ *            ("FlashAttention-3 on Hopper", section 5.6.1). Hkv = 1 is MQA.
+ *   Dense    cu_seqlens_q = cu_seqlens_k = NULL: q, o are [B, Nq, Hq, d],
+ *            k, v are [B, Nk, Hkv, d], lse is float32 [B, Hq, Nq];
+ *            total_q and total_k are ignored.
+ *   Packed   cu_seqlens_q, cu_seqlens_k: device int32 arrays of B + 1 row
+ *            offsets (sequence b owns rows cu[b] .. cu[b+1]-1; the pages
+ *            list variable-length batches in chapter 9.3, whose text is
+ *            missing): q, o are [total_q, Hq, d], k, v are [total_k, Hkv, d],
+ *            lse is float32 [Hq, total_q]. Nq and Nk are the largest sequence
+ *            lengths (they size the grid; longer sequences are cut to them).
+ *            Offsets are clamped into [0, total] on the device, so malformed
+ *            arrays never address outside the tensors, but rows that no valid
+ *            sequence covers are left unspecified.
+ *   causal   1: query i of a sequence sees key j iff j <= i + (N_k - N_q)
+ *            (bottom-right alignment, section 4.7); a row that sees no key
+ *            gets O = 0 and LSE = -inf. With N_q = 1 this is every key.
+ *   pack_gqa 1: the g = Hq / Hkv query heads of one key/value head share a
+ *            128-row query tile (rows interleave as query-major, head-minor),
+ *            so a K/V tile is read once for the group; 0: one query head per
+ *            tile; -1: attn_pack_gqa_heuristic decides. The pages list this as
+ *            PackGQA (chapter 11, text missing). The result does not depend on
+ *            the choice. When Nq * g <= 16 and d <= 128 (decode) a kernel for
+ *            few rows runs instead, which always packs the group and ignores
+ *            pack_gqa.
+ *   num_splits  >= 1. With more than one range the keys are cut into
+ *            consecutive ranges of split_len = 64 * ceil(ceil(Nk / num_splits)
+ *            / 64) keys (the last may be shorter; empty ranges are dropped, so
+ *            at most num_splits are used). Each range writes its normalised
+ *            state O_s = O~_s / l_s, LSE_s = m_s + ln l_s to the workspace
+ *            (float32 [S, total_q, Hq, d] then [S, total_q, Hq], S the ranges
+ *            used; total_q = B * Nq for dense inputs) and a second kernel
+ *            merges them, LSE = ln sum_s e^(LSE_s), O = sum_s e^(LSE_s - LSE)
+ *            O_s (the block-combine rule, section 3.2.1; split-KV, chapter 10).
+ *   workspace  caller-owned device memory of at least
+ *            attn_splitkv_workspace_bytes(num_splits, total_q, Hq, d) bytes,
+ *            16-byte aligned, not overlapping any other argument; unused (may
+ *            be NULL) when one range is used.
+ *   Other arguments, errors and the rounding as attn_fwd. Empty problems
+ *   (B, Hq, Nq or total_q = 0) are no-ops; Nk = 0 (or an empty key sequence)
+ *   gives O = 0 and LSE = -inf for its rows.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q, int total_k,
+                int causal, float alpha, int dtype, int pack_gqa, int num_splits,
+                float* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_ex needs for num_splits key ranges (0 for
+ * num_splits <= 1): num_splits * total_q * Hq * (d + 1) * 4. */
+int64_t attn_splitkv_workspace_bytes(int num_splits, int total_q, int Hq, int d);
+
+/* 1 if packing the query heads of a group takes fewer 128-row query tiles
+ * than one head per tile (e.g. decode with Nq = 1 and Hq > Hkv), else 0. */
+int attn_pack_gqa_heuristic(int Hq, int Hkv, int Nq);
+
+/* Suggested num_splits for attn_fwd_ex on a device with num_cus compute
+ * units. With Nq * Hq / Hkv <= 16 query rows per key/value head and d <= 128
+ * (decode) the call runs a kernel with one workgroup per (sequence,
+ * key/value head, range): enough ranges for about num_cus workgroups, at
+ * least 512 keys each. Otherwise: 1 when the 128-row query tiles alone fill
+ * every resident workgroup slot (two per compute unit for d <= 128, one for
+ * d = 256), else enough ranges to fill them, at least 256 keys each. At most
+ * 128 ranges. pack_gqa as in attn_fwd_ex. */
+int attn_num_splits_heuristic(int B, int Hq, int Hkv, int Nq, int Nk, int d, int pack_gqa, int num_cus);
+
 /* Message of the last failed call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */
 const char* attn_last_error(void);

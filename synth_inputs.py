@@ -15,6 +15,11 @@ Hopper", section 6.4):
 * The upstream gradient dO of the backward is drawn from its own generator,
   ``default_rng([seed, 1])``, as one ``standard_normal((B, N, H, d), float32)``
   draw rounded the same way, so it does not disturb the Q, K, V stream.
+* Grouped heads / N_q != N_k (``make_qkv_gqa``): the same generator and
+  order, with Q drawn as (B, N_q, H_q, d) and K, V as (B, N_k, H_kv, d).
+* Packed variable-length batches (``make_seqlens``): per-sequence lengths
+  i.i.d. uniform on [lo, hi] from ``default_rng([seed, 2])``; the packed
+  tensors are ``make_qkv_gqa`` draws with B = 1 and N = the total length.
 * Outliers (optional): an i.i.d. Bernoulli(rate) mask per element, independent
   for Q, K and V, drawn from the same generator after the base draws.
   ``kind="scale"`` multiplies the selected entries by ``factor`` (10);
@@ -33,6 +38,8 @@ __all__ = [
     "make_qkv",
     "make_qkv_f32",
     "make_dout",
+    "make_qkv_gqa",
+    "make_seqlens",
 ]
 
 
@@ -128,3 +135,33 @@ def make_dout(B, N, H, d, seed=0, dtype="bf16"):
         bits = f32_to_f16_bits(g)
         return bits, f16_bits_to_f32(bits).astype(np.float64)
     raise ValueError(dtype)
+
+
+def _round16(x, dtype):
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+    if dtype == "f16":
+        bits = f32_to_f16_bits(x)
+        return bits, f16_bits_to_f32(bits).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def make_qkv_gqa(B, Nq, Nk, Hq, Hkv, d, seed=0, dtype="bf16"):
+    """Q (B, Nq, Hq, d) and K, V (B, Nk, Hkv, d), drawn in that order from
+    ``default_rng(seed)`` and rounded like ``make_qkv``: (bits, values)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Nq, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((B, Nk, Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((B, Nk, Hkv, d), dtype=np.float32)
+    pairs = [_round16(t, dtype) for t in (q, k, v)]
+    return tuple(p[0] for p in pairs), tuple(p[1] for p in pairs)
+
+
+def make_seqlens(B, lo, hi, seed=0):
+    """B sequence lengths, i.i.d. uniform integers on [lo, hi], and their
+    prefix offsets (B + 1 int32 values starting at 0)."""
+    rng = np.random.default_rng([seed, 2])
+    lens = rng.integers(lo, hi + 1, size=B).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return lens, cu

@@ -156,6 +156,79 @@ def test_bwd_empty_problem_is_a_no_op():
     assert _bwd(B=0) == ea.ATTN_OK
 
 
+def _ex(**kw):
+    lib = ea.load()
+    a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000, lse=FAKE + 0x40000000,
+             B=2, Hq=8, Hkv=2, Nq=1, Nk=1000, d=128, cu_q=None, cu_k=None, total_q=0, total_k=0, causal=1,
+             alpha=0.1, dtype=0, pack=-1, splits=1, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                           a["d"], a["cu_q"], a["cu_k"], a["total_q"], a["total_k"], a["causal"], a["alpha"],
+                           a["dtype"], a["pack"], a["splits"], a["ws"], ctypes.c_int64(a["ws_bytes"]), a["stream"])
+
+
+WS = FAKE + 0x60000000
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(Hkv=0), ea.ATTN_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(splits=0), ea.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(pack=2), ea.ATTN_ERR_INVALID_ARG, "pack_gqa"),
+    (dict(d=80), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(dtype=5), ea.ATTN_ERR_UNSUPPORTED, "dtype"),
+    (dict(Nk=-1), ea.ATTN_ERR_INVALID_ARG, ">= 0"),
+    (dict(splits=4), ea.ATTN_ERR_INVALID_ARG, "workspace is null"),
+    (dict(splits=4, ws=WS, ws_bytes=100), ea.ATTN_ERR_INVALID_ARG, "workspace has 100 bytes"),
+    (dict(splits=4, ws=WS + 4, ws_bytes=1 << 20), ea.ATTN_ERR_INVALID_ARG, "workspace is not 16-byte"),
+    (dict(splits=4, ws=FAKE + 0x100, ws_bytes=1 << 20), ea.ATTN_ERR_INVALID_ARG, "workspace overlaps q"),
+    (dict(cu_q=FAKE + 0x70000000), ea.ATTN_ERR_INVALID_ARG, "both"),
+    (dict(cu_q=FAKE + 0x70000002, cu_k=FAKE + 0x70001000, total_q=5, total_k=9), ea.ATTN_ERR_INVALID_ARG,
+     "4-byte"),
+    (dict(cu_q=FAKE + 0x70000000, cu_k=FAKE + 0x70001000, total_q=-1, total_k=9), ea.ATTN_ERR_INVALID_ARG,
+     "total_q"),
+    (dict(o=FAKE + 0x10000000), ea.ATTN_ERR_INVALID_ARG, "o overlaps k"),
+    (dict(Nk=1 << 20, Hkv=8, Hq=8, d=256), ea.ATTN_ERR_UNSUPPORTED, "too long"),
+])
+def test_fwd_ex_rejects_bad_arguments_before_launch(kw, status, msg):
+    assert _ex(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def test_fwd_ex_empty_problems_and_single_range_need_no_workspace():
+    for kw in (dict(B=0), dict(Nq=0), dict(Hq=0),
+               dict(cu_q=FAKE + 0x70000000, cu_k=FAKE + 0x70001000, total_q=0, total_k=9)):
+        assert _ex(**kw) == ea.ATTN_OK, kw
+    # splits = 4 over Nk = 64 keys is a single range of 64: no workspace needed,
+    # so validation passes it to the launch (not run here: Nq = 0 keeps it empty)
+    assert _ex(splits=4, Nk=64, Nq=0) == ea.ATTN_OK
+
+
+def test_split_and_pack_sizing_helpers():
+    # workspace: num_splits * total_q * Hq * (d + 1) floats
+    assert ea.attn_splitkv_workspace_bytes(4, 10, 8, 128) == 4 * 10 * 8 * 129 * 4
+    assert ea.attn_splitkv_workspace_bytes(1, 10, 8, 128) == 0
+    # packing pays when it needs fewer 128-row tiles
+    assert ea.attn_pack_gqa_heuristic(64, 8, 1) == 1
+    assert ea.attn_pack_gqa_heuristic(64, 8, 100) == 1
+    assert ea.attn_pack_gqa_heuristic(64, 8, 128) == 0
+    assert ea.attn_pack_gqa_heuristic(8, 8, 1) == 0
+    # decode (8 query rows per KV head): 8 x 8 (sequence, KV head) units on
+    # 256 CUs, aiming at 256 workgroups: 4 ranges; capped at one range per
+    # 512 keys and at 128 ranges
+    assert ea.attn_num_splits_heuristic(8, 64, 8, 1, 8192, 128, -1, 256) == 4
+    assert ea.attn_num_splits_heuristic(1, 32, 8, 1, 8192, 128, -1, 256) == 16
+    assert ea.attn_num_splits_heuristic(8, 64, 8, 1, 1000, 128, -1, 256) == 2
+    assert ea.attn_num_splits_heuristic(1, 1, 1, 1, 1 << 20, 128, -1, 256) == 128
+    assert ea.attn_num_splits_heuristic(64, 8, 8, 1, 8192, 128, -1, 256) == 1
+    # d = 256 decode stays on the tiled kernel (1 x 2 heads x 1 tile = 2
+    # workgroups, 256 slots, at least 256 keys per range)
+    assert ea.attn_num_splits_heuristic(1, 2, 2, 1, 8192, 256, -1, 256) == 32
+    # tiled kernel: 1 x 8 heads of 4 query tiles = 32 workgroups, 512 slots
+    assert ea.attn_num_splits_heuristic(1, 8, 8, 512, 8192, 128, -1, 256) == 16
+    assert ea.attn_num_splits_heuristic(2, 16, 16, 8192, 8192, 128, -1, 256) == 1
+
+
 def test_binding_has_no_cpu_fallback(monkeypatch):
     # with the library path pointing nowhere the binding must raise, not compute
     monkeypatch.setattr(ea, "lib_path", "/nonexistent/libattn.so")
