@@ -51,7 +51,7 @@ def causal_mask(nq: int, nk: int) -> np.ndarray:
     return cols > rows + (nk - nq)
 
 
-def attention_head(q, k, v, alpha, causal=False, row_chunk=1024, rows=None):
+def attention_head(q, k, v, alpha, causal=False, row_chunk=1024, rows=None, mask=None):
     """One (batch, head): q (Nq, d), k (Nk, d), v (Nk, dv) -> (O, LSE).
 
     Follows the plain definition row by row ("FlashAttention-3 paper review",
@@ -68,7 +68,8 @@ def attention_head(q, k, v, alpha, causal=False, row_chunk=1024, rows=None):
 
     ``rows`` optionally selects query rows (an index array); the result then
     has one row per selected index. Rows are processed ``row_chunk`` at a time
-    so S never needs more than row_chunk * Nk doubles.
+    so S never needs more than row_chunk * Nk doubles. ``mask``, when given,
+    is a further (Nq, Nk) boolean array of excluded entries (step 2).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -86,6 +87,8 @@ def attention_head(q, k, v, alpha, causal=False, row_chunk=1024, rows=None):
         s = float(alpha) * (q[sel] @ k.T)
         if causal:
             s = np.where(causal_mask(nq, nk)[sel], -np.inf, s)
+        if mask is not None:
+            s = np.where(np.asarray(mask, dtype=bool)[sel], -np.inf, s)
         m = s.max(axis=1)
         live = np.isfinite(m)
         m_safe = np.where(live, m, 0.0)

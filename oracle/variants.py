@@ -16,6 +16,12 @@ Sources (pages on FlashAttention-3):
   (sequence b owns rows cu[b] .. cu[b+1]-1), and each sequence is an
   independent attention problem with its own N_q, N_k and causal offset.
   LSE is laid out (H_q, total_q).
+* local (sliding-window) attention: section 4.7 of the same page says a
+  window adds a left boundary to the causal right one; its text gives no
+  formula. Reading taken here, with the same bottom-right alignment
+  (off = N_k - N_q): query i sees key j iff
+  i + off - w_left <= j <= i + off + w_right, a negative width meaning no
+  bound on that side; the causal flag is the right bound 0.
 * split-KV: section 3.2.1 (the block-combine rule merges the states of
   disjoint key sets) and chapter 10 (split-KV, body missing). Reading taken
   here: the keys are cut into consecutive ranges; the state of one range is
@@ -35,7 +41,21 @@ import numpy as np
 
 from .attention import attention_head, causal_mask
 
-__all__ = ["attention_gqa", "attention_varlen", "split_states", "merge_lse_states"]
+__all__ = ["window_mask", "attention_gqa", "attention_varlen", "split_states", "merge_lse_states"]
+
+
+def window_mask(nq, nk, window_left=-1, window_right=-1):
+    """(nq, nk) boolean array, True where key j lies outside the window of
+    query i: j < i + off - window_left or j > i + off + window_right, with
+    off = nk - nq; a negative width leaves that side unbounded."""
+    rows = np.arange(nq)[:, None] + (nk - nq)
+    cols = np.arange(nk)[None, :]
+    out = np.zeros((nq, nk), dtype=bool)
+    if window_left >= 0:
+        out |= cols < rows - window_left
+    if window_right >= 0:
+        out |= cols > rows + window_right
+    return out
 
 
 def _group(hq: int, hkv: int) -> int:
@@ -44,8 +64,9 @@ def _group(hq: int, hkv: int) -> int:
     return hq // hkv
 
 
-def attention_gqa(q, k, v, alpha=None, causal=False):
-    """Dense forward with H_q query heads over H_kv key/value heads."""
+def attention_gqa(q, k, v, alpha=None, causal=False, window=(-1, -1)):
+    """Dense forward with H_q query heads over H_kv key/value heads;
+    ``window`` = (w_left, w_right) as in ``window_mask``."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -56,14 +77,16 @@ def attention_gqa(q, k, v, alpha=None, causal=False):
         alpha = 1.0 / np.sqrt(d)
     o = np.zeros((B, nq, hq, v.shape[3]))
     lse = np.zeros((B, hq, nq))
+    mask = window_mask(nq, k.shape[1], *window)
     for b in range(B):
         for h in range(hq):
             kh = h // g  # section 5.6.1: KV head floor(h / g)
-            o[b, :, h], lse[b, h] = attention_head(q[b, :, h], k[b, :, kh], v[b, :, kh], alpha, causal)
+            o[b, :, h], lse[b, h] = attention_head(q[b, :, h], k[b, :, kh], v[b, :, kh], alpha, causal,
+                                                   mask=mask)
     return o, lse
 
 
-def attention_varlen(q, k, v, cu_q, cu_k, alpha=None, causal=False):
+def attention_varlen(q, k, v, cu_q, cu_k, alpha=None, causal=False, window=(-1, -1)):
     """Packed variable-length forward: sequence b is rows cu[b] .. cu[b+1]-1."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -82,9 +105,11 @@ def attention_varlen(q, k, v, cu_q, cu_k, alpha=None, causal=False):
         k0, k1 = cu_k[b], cu_k[b + 1]
         if q1 == q0:
             continue
+        mask = window_mask(q1 - q0, k1 - k0, *window)
         for h in range(hq):
             kh = h // g
-            o[q0:q1, h], lse[h, q0:q1] = attention_head(q[q0:q1, h], k[k0:k1, kh], v[k0:k1, kh], alpha, causal)
+            o[q0:q1, h], lse[h, q0:q1] = attention_head(q[q0:q1, h], k[k0:k1, kh], v[k0:k1, kh], alpha, causal,
+                                                        mask=mask)
     return o, lse
 
 

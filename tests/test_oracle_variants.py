@@ -11,8 +11,8 @@ form of the combine rule, pinned in test_oracle.py).
 import numpy as np
 import pytest
 
-from oracle.attention import attention, attention_head, combine
-from oracle.variants import attention_gqa, attention_varlen, merge_lse_states, split_states
+from oracle.attention import attention, attention_head, causal_mask, combine
+from oracle.variants import attention_gqa, attention_varlen, merge_lse_states, split_states, window_mask
 
 
 def _rand(shape, seed):
@@ -153,3 +153,52 @@ def test_lse_merge_agrees_with_state_combine():
     o, lse = merge_lse_states(op, lp)
     np.testing.assert_allclose(o, ot / l[:, None], rtol=1e-13)
     np.testing.assert_allclose(lse, m + np.log(l), rtol=1e-13)
+
+
+def test_window_mask_by_hand():
+    # N_q = 3, N_k = 5 (off = 2), window (1, 0): row i sees keys i+1 .. i+2
+    m = window_mask(3, 5, 1, 0)
+    expect = np.array([[1, 0, 0, 1, 1],
+                       [1, 1, 0, 0, 1],
+                       [1, 1, 1, 0, 0]], dtype=bool)
+    np.testing.assert_array_equal(m, expect)
+    # unbounded left, right bound 0: the causal mask
+    np.testing.assert_array_equal(window_mask(4, 7, -1, 0), causal_mask(4, 7))
+    # both unbounded: nothing excluded
+    assert not window_mask(3, 5).any()
+
+
+def test_window_zero_width_picks_the_diagonal_key():
+    # window (0, 0): query i sees only key i + off, so O_i = V_{i+off} and
+    # LSE_i = alpha q_i . k_{i+off}
+    B, nq, nk, h, d = 1, 4, 9, 2, 5
+    q, k, v = _rand((B, nq, h, d), 24), _rand((B, nk, h, d), 25), _rand((B, nk, h, d), 26)
+    o, lse = attention_gqa(q, k, v, 0.3, False, window=(0, 0))
+    off = nk - nq
+    for i in range(nq):
+        np.testing.assert_allclose(o[0, i], v[0, i + off], rtol=1e-14)
+        for hh in range(h):
+            np.testing.assert_allclose(lse[0, hh, i], 0.3 * q[0, i, hh] @ k[0, i + off, hh], rtol=1e-13)
+
+
+def test_window_brute_force_and_limits():
+    nq, nk, d = 6, 10, 3
+    q, k, v = _rand((1, nq, 1, d), 27), _rand((1, nk, 1, d), 28), _rand((1, nk, 1, d), 29)
+    wl, wr = 2, 1
+    o, lse = attention_gqa(q, k, v, 0.5, False, window=(wl, wr))
+    off = nk - nq
+    for i in range(nq):
+        keys = [j for j in range(nk) if i + off - wl <= j <= i + off + wr]
+        s = [0.5 * sum(q[0, i, 0, t] * k[0, j, 0, t] for t in range(d)) for j in keys]
+        mx = max(s)
+        w = [np.exp(x - mx) for x in s]
+        ref = [sum(w[a] * v[0, j, 0, t] for a, j in enumerate(keys)) / sum(w) for t in range(d)]
+        np.testing.assert_allclose(o[0, i, 0], ref, rtol=1e-12)
+    # a window wider than the sequence is full attention; causal with a
+    # right window is the causal result
+    o1, l1 = attention_gqa(q, k, v, 0.5, False, window=(nk, nk))
+    o2, l2 = attention_gqa(q, k, v, 0.5, False)
+    np.testing.assert_allclose(o1, o2, rtol=1e-14)
+    o3, _ = attention_gqa(q, k, v, 0.5, True, window=(-1, 3))
+    o4, _ = attention_gqa(q, k, v, 0.5, True)
+    np.testing.assert_allclose(o3, o4, rtol=1e-14)
