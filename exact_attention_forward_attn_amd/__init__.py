@@ -85,7 +85,7 @@ def load():
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_bwd.restype = i
-    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, f, i, i, i, vp,
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, i, i, f, i, i, i, vp,
                                 ctypes.c_int64, vp]
     lib.attn_fwd_ex.restype = i
     lib.attn_splitkv_workspace_bytes.argtypes = [i, i, i, i]
@@ -195,8 +195,10 @@ def _ex_shapes(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k):
 
 
 def attn_fwd_ex(q, k, v, o, lse, causal=False, alpha=None, cu_seqlens_q=None, cu_seqlens_k=None,
-                max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, workspace=None, stream=None):
-    """Forward with grouped heads, N_q != N_k, packed batches and split-KV."""
+                max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, workspace=None, stream=None,
+                window=(-1, -1)):
+    """Forward with grouped heads, N_q != N_k, packed batches, split-KV and a
+    (left, right) sliding window (-1 = unbounded side)."""
     torch = _torch()
     lib = load()
     if q.dtype not in (torch.bfloat16, torch.float16):
@@ -222,13 +224,14 @@ def attn_fwd_ex(q, k, v, o, lse, causal=False, alpha=None, cu_seqlens_q=None, cu
         ws, ws_bytes = _ptr(workspace), workspace.numel() * 4
     dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
     _check(lib.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, cu_q, cu_k,
-                           total_q, total_k, int(bool(causal)), _default_alpha(d, alpha), dt, int(pack_gqa),
+                           total_q, total_k, int(bool(causal)), int(window[0]), int(window[1]),
+                           _default_alpha(d, alpha), dt, int(pack_gqa),
                            int(num_splits), ws, ctypes.c_int64(ws_bytes), _stream_handle(stream)))
     return o, lse
 
 
 def attention_ex(q, k, v, causal=False, alpha=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
-                 max_seqlen_k=None, pack_gqa=-1, num_splits=None, stream=None):
+                 max_seqlen_k=None, pack_gqa=-1, num_splits=None, stream=None, window=(-1, -1)):
     """Allocate O, LSE and the split-KV workspace with torch and run attn_fwd_ex.
 
     ``num_splits=None`` takes attn_num_splits_heuristic for this device.
@@ -244,7 +247,7 @@ def attention_ex(q, k, v, causal=False, alpha=None, cu_seqlens_q=None, cu_seqlen
     nbytes = attn_splitkv_workspace_bytes(num_splits, total_q, Hq, d)
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device) if nbytes else None
     return attn_fwd_ex(q, k, v, o, lse, causal, alpha, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                       pack_gqa, num_splits, ws, stream)
+                       pack_gqa, num_splits, ws, stream, window)
 
 
 def attn_fp8_prepare(x, x8, descale, block_rows=128, hadamard=False, seed=0, stream=None):

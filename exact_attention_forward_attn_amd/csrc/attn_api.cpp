@@ -118,6 +118,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.scale_log2 = scale_log2(alpha);
   a.Hkv = H; a.Nk = N;
   a.total_q = a.total_k = B * N;
+  a.win_l = 2 * N + 1;  // unbounded left
+  a.win_r = 0;          // causal (used only when causal = 1)
   a.nsplit = 1;
   return hip_status(attn::launch_fwd_16(a, stream), "attn_fwd launch");
 }
@@ -161,8 +163,8 @@ int attn_num_splits_heuristic(int B, int Hq, int Hkv, int Nq, int Nk, int d, int
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                 int Nq, int Nk, int d, const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q,
-                int total_k, int causal, float alpha, int dtype, int pack_gqa, int num_splits,
-                float* workspace, int64_t workspace_bytes, void* stream) {
+                int total_k, int causal, int window_left, int window_right, float alpha, int dtype,
+                int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes, void* stream) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
@@ -173,6 +175,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0))
     return fail(ATTN_ERR_INVALID_ARG, "Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (window_left < -1 || window_right < -1)
+    return fail(ATTN_ERR_INVALID_ARG, "window widths must be >= -1 (got %d, %d)", window_left, window_right);
   if (!std::isfinite(alpha) || alpha < 0.f)
     return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
   if (pack_gqa < -1 || pack_gqa > 1) return fail(ATTN_ERR_INVALID_ARG, "pack_gqa must be -1, 0 or 1");
@@ -242,7 +246,13 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   attn::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.B = B; a.H = Hq; a.N = Nq; a.d = d;
-  a.causal = causal;
+  // the masked kernels take the window; causal is its right width 0, and an
+  // unbounded side is any width past the sequence (Nq + Nk + 1)
+  const int wide = Nq + Nk + 1;
+  a.win_l = window_left < 0 ? wide : (window_left < wide ? window_left : wide);
+  a.win_r = window_right < 0 ? wide : (window_right < wide ? window_right : wide);
+  if (causal) a.win_r = 0;
+  a.causal = (causal || window_left >= 0 || window_right >= 0) ? 1 : 0;
   a.dtype = dtype;
   a.scale_log2 = scale_log2(alpha);
   a.Hkv = Hkv; a.Nk = Nk;

@@ -60,7 +60,8 @@ struct Args {
   int Nq, Nk;
   int total_q, total_k;
   int nsplit, split_len;
-  float c;  // alpha * log2(e)
+  int win_l, win_r;  // window widths (masked kernels; wide = unbounded)
+  float c;           // alpha * log2(e)
 };
 
 template <int D>
@@ -185,10 +186,18 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
   // ---- key range and this wave's tiles ---------------------------------------
   const int kb0 = split * a.split_len;
   const int kb1 = min(len_k, kb0 + a.split_len);
-  // (causal masking never shortens the range: with bottom-right alignment
-  // the last query row of a sequence sees every key)
+  // (the right bound never shortens the range: with bottom-right alignment
+  // the last query row of a sequence sees every key up to len_k - 1 + win_r)
+  // masked instantiation: query n sees key j iff
+  // n + off - win_l <= j <= n + off + win_r; tiles left of the first row's
+  // window are skipped (t0)
   const int nt = kb1 > kb0 ? (kb1 - kb0 + G::BN - 1) / G::BN : 0;
-  const int cnt = nt > wave ? (nt - wave + NW - 1) / NW : 0;
+  int t0 = 0;
+  if (CAUSAL) {
+    const int lo = off - a.win_l;  // first key of row 0's window
+    if (lo > kb0) t0 = min((lo - kb0) / G::BN, nt);
+  }
+  const int cnt = nt - t0 > wave ? (nt - t0 - wave + NW - 1) / NW : 0;
   auto stage = [&](auto st_tag) ATTN_INLINE -> char* {
     return (decltype(st_tag)::value ? ring1 : ring0) + wave * G::TILE;
   };
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
   // x%CPR, which holds logical chunk (x%CPR) ^ swizzle(row).
   auto issue = [&](auto st_tag, int i) ATTN_INLINE {
     constexpr int ST = decltype(st_tag)::value;
-    const int kv0 = kb0 + (wave + NW * i) * G::BN;
+    const int kv0 = kb0 + (t0 + wave + NW * i) * G::BN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -239,7 +248,7 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) pin(qreg[kc]);
     const LDS_AS char* vt = (const LDS_AS char*)stage(st_tag);
-    const int kv0 = kb0 + (wave + NW * i) * G::BN;
+    const int kv0 = kb0 + (t0 + wave + NW * i) * G::BN;
 
     // S^T for keys kv0 + 16 kb + 4 grp + e (e = 0..3), row l16
     f32x4 s[2];
@@ -252,12 +261,15 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = s[e / 4][e % 4] * c;
-    // keys at or past kb1, and (causal) right of the row's diagonal
-    if (kv0 + G::BN > kb1 || (CAUSAL && kv0 + G::BN - 1 > off)) {
+    // keys at or past kb1, and (masked) outside the row's window; rows
+    // 0 .. len_q-1 bound which tiles can need it
+    if (kv0 + G::BN > kb1 ||
+        (CAUSAL && (kv0 + G::BN - 1 > off + a.win_r || kv0 < len_q - 1 + off - a.win_l))) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int key = kv0 + 16 * (e / 4) + 4 * grp + (e % 4);
-        if (key >= kb1 || (CAUSAL && key > n_r + off)) x[e] = -__builtin_inff();
+        if (key >= kb1 || (CAUSAL && (key > n_r + off + a.win_r || key < n_r + off - a.win_l)))
+          x[e] = -__builtin_inff();
       }
     }
     float mx = x[0];
@@ -395,6 +407,8 @@ int launch(const FwdArgs& f, hipStream_t st) {
   a.total_q = f.total_q; a.total_k = f.total_k;
   a.nsplit = f.nsplit > 1 ? f.nsplit : 1;
   a.split_len = f.nsplit > 1 ? f.split_len : 0x7fffffff;
+  a.win_l = f.win_l;
+  a.win_r = f.win_r;
   a.c = f.scale_log2;
   const int grid = f.B * f.Hkv * a.nsplit;
   hipLaunchKernelGGL((decode_kernel<D, CAUSAL, T>), dim3(grid), dim3(DGeo<D>::NW * 64), 0, st, a);

@@ -75,6 +75,7 @@ struct KernelArgs {
   int n_mblk;         // query blocks per (batch entry, head unit)
   int nunit;          // B * hu
   int nsplit, split_len;
+  int win_l, win_r;   // window widths (masked kernels; wide = unbounded)
   float c;            // alpha * log2(e)
 };
 
@@ -188,7 +189,7 @@ void fwd_kernel(KernelArgs a) {
   }
 
   // last key of this lane's row, less the lane's key offset in a tile
-  const int diag = n_i + off - 4 * h32;
+  const int diag = n_i + off + a.win_r - 4 * h32;
 
   // ---- per-lane LDS offsets -------------------------------------------------
   // global -> LDS copy: segment seg = wave + 4t, lane i covers row seg*RPS +
@@ -242,27 +243,38 @@ void fwd_kernel(KernelArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
 
-  // Keys of this workgroup: its key range [kb0, kb1), cut short (causal) at
-  // the last key its last query sees. Query n sees key j iff
-  // j <= n + (len_k - len_q) ("FlashAttention-3 on Hopper", section 4.7).
+  // Keys of this workgroup: its key range [kb0, kb1), cut to the keys some
+  // query of the workgroup sees. In the masked instantiation query n sees
+  // key j iff n + off - win_l <= j <= n + off + win_r: causal is win_r = 0
+  // with an unbounded left side (bottom-right alignment, "FlashAttention-3
+  // on Hopper", section 4.7, which also names the left boundary of local
+  // attention).
   const int kb0 = split * a.split_len;
   const int kb1 = min(len_k, kb0 + a.split_len);
-  int kv_end = kb1;
+  int kv_end = kb1, kbase = kb0;
   if (CAUSAL) {
+    const int n_first = pack ? q0 / grp : q0;
     const int n_last = min(len_q - 1, pack ? (q0 + BM - 1) / grp : q0 + BM - 1);
-    kv_end = min(kv_end, n_last + off + 1);
+    kv_end = min(kv_end, n_last + off + a.win_r + 1);
+    const int lo = n_first + off - a.win_l;  // first key the workgroup sees
+    if (lo > kb0) kbase = kb0 + (min(lo, kb1) - kb0) / BN * BN;
   }
-  const int nt = kv_end > kb0 ? (kv_end - kb0 + BN - 1) / BN : 0;
+  const int nt = kv_end > kbase ? (kv_end - kbase + BN - 1) / BN : 0;
   // Processing order i = 0 .. nt-1 visits KV tile j = nt-1-i (descending;
-  // tile j starts at key kb0 + j*BN). The tiles this wave must mask (keys at
-  // or past kb1, keys right of its diagonal) form a prefix of that order:
-  // tile j is masked iff j >= jm.
-  int jm = kb1 - kb0 >= BN ? (kb1 - kb0 - BN) / BN + 1 : 0;
+  // tile j starts at key kbase + j*BN). The tiles this wave must mask on the
+  // right (keys at or past kb1, keys right of its diagonal) form a prefix of
+  // that order: tile j is masked iff j >= jm. Tiles holding keys left of a
+  // row's window form a suffix: processing index i >= left_from.
+  int jm = kb1 - kbase >= BN ? (kb1 - kbase - BN) / BN + 1 : 0;
+  int left_from = nt;
   if (CAUSAL) {
-    const int x = (pack ? qw / grp : qw) + off - kb0 - BN + 1;
+    const int x = (pack ? qw / grp : qw) + off + a.win_r - kbase - BN + 1;
     jm = min(jm, x >= 0 ? x / BN + 1 : 0);
+    const int lw = (pack ? (qw + 31) / grp : qw + 31) + off - a.win_l;  // the wave's last left bound
+    if (lw > kbase) left_from = max(0, nt - (lw - kbase + BN - 1) / BN);
   }
   const int n_masked = max(0, nt - jm);
+  const int wsum = a.win_l + a.win_r;
 
   // Tile i (processing order) lives in slot i % 2.
   auto kslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? kbuf1 : kbuf0; };
@@ -272,7 +284,7 @@ void fwd_kernel(KernelArgs a) {
   // the VGPR offset: the buffer range check, which zero-fills rows past N,
   // does not cover the scalar offset.)
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) ATTN_INLINE {
-    const uint32_t base = (uint32_t)(kb0 + (nt - 1 - i) * BN) * RSK;
+    const uint32_t base = (uint32_t)(kbase + (nt - 1 - i) * BN) * RSK;
     const uint32_t g0 = is_k ? kg[0] : vg0;
     const uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
 #pragma unroll
@@ -305,20 +317,22 @@ void fwd_kernel(KernelArgs a) {
     }
   };
 
-  // Scores of keys at or past kb1 or right of the diagonal become -inf (only
-  // the tiles of the masked prefix call this). kv0: first key of the tile.
+  // Scores of keys at or past kb1, right of the diagonal or left of the
+  // window become -inf (only the tiles of the masked prefix and suffix call
+  // this). kv0: first key of the tile.
   auto apply_mask = [&](auto sb_tag, int kv0) ATTN_INLINE {
     constexpr int SB = decltype(sb_tag)::value;
     // key offset within the tile = 4*h32 + o with o a compile-time constant,
     // so compare o against per-lane thresholds (no per-element index vectors)
     const int tn = kb1 - kv0 - 4 * h32;        // o >= tn: key at or past kb1
-    const int tc = diag - kv0;                 // o > tc: key right of the diagonal
+    const int tc = diag - kv0;                 // o > tc: key right of the window
+    const int tl = tc - wsum;                  // o < tl: key left of the window
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
-        if (o >= tn || (CAUSAL && o > tc)) s[SB][kb][r] = -__builtin_inff();
+        if (o >= tn || (CAUSAL && (o > tc || o < tl))) s[SB][kb][r] = -__builtin_inff();
       }
   };
 
@@ -501,8 +515,8 @@ void fwd_kernel(KernelArgs a) {
   if (nt > 1) qk(Int<1>{}, kbuf1);
   barrier();  // every wave has read K_0
   if (nt > 2) issue(rk, true, kbuf0, 2);
-  if (n_masked > 0) apply_mask(Int<0>{}, kb0 + (nt - 1) * BN);
-  if (n_masked > 1) apply_mask(Int<1>{}, kb0 + (nt - 2) * BN);
+  if (n_masked > 0 || left_from == 0) apply_mask(Int<0>{}, kbase + (nt - 1) * BN);
+  if (nt > 1 && (n_masked > 1 || left_from <= 1)) apply_mask(Int<1>{}, kbase + (nt - 2) * BN);
   {
     constexpr Sched S0{16};
     For<0, S0.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<16>{}, TrueT{}); });
@@ -519,7 +533,8 @@ void fwd_kernel(KernelArgs a) {
     if (i + 1 < nt) issue(rv, false, vslot(Int<J + 1>{}), i + 1);
     if (i + 3 < nt) issue(rk, true, kslot(Int<J + 1>{}), i + 3);
     block(j_tag, qk_tag, sm_tag);
-    if (decltype(qk_tag)::value && i + 2 < n_masked) apply_mask(Int<J>{}, kb0 + (nt - 3 - i) * BN);
+    if (decltype(qk_tag)::value && (i + 2 < n_masked || i + 2 >= left_from))
+      apply_mask(Int<J>{}, kbase + (nt - 3 - i) * BN);
   };
   // unrolled by two (the trip count is uniform over the workgroup), which
   // makes every slot and buffer index a compile-time constant
@@ -680,6 +695,8 @@ int launch(const FwdArgs& f, hipStream_t st) {
   a.nunit = f.B * a.hu;
   a.nsplit = f.nsplit > 1 ? f.nsplit : 1;
   a.split_len = f.nsplit > 1 ? f.split_len : 0x7fffffff;
+  a.win_l = f.win_l;
+  a.win_r = f.win_r;
   a.c = f.scale_log2;
   const int grid = a.n_mblk * a.nunit * a.nsplit;
   hipLaunchKernelGGL((fwd_kernel<D, KB, CAUSAL, T>), dim3(grid), dim3(256), 0, st, a);

@@ -31,6 +31,9 @@ struct FwdArgs {
   int total_q;       // rows of q and o (B * N for dense inputs)
   int total_k;       // rows of k and v
   int pack;          // query heads of one key/value head share a tile
+  int win_l, win_r;  // masked path (causal = 1): query n sees key j iff
+                     // n + off - win_l <= j <= n + off + win_r, off = Nk - Nq
+                     // (widths >= 0; "unbounded" is passed as Nq + Nk + 1)
   int nsplit;        // key ranges (1: no split)
   int split_len;     // keys per range, a multiple of 64
   float* opart;      // nsplit > 1: [nsplit, total_q, H, d] float32 partial O

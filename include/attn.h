@@ -181,6 +181,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  *   causal   1: query i of a sequence sees key j iff j <= i + (N_k - N_q)
  *            (bottom-right alignment, section 4.7); a row that sees no key
  *            gets O = 0 and LSE = -inf. With N_q = 1 this is every key.
+ *   window_left, window_right  local (sliding-window) attention, >= -1:
+ *            query i sees key j iff i + off - window_left <= j and
+ *            j <= i + off + window_right, off = N_k - N_q; -1 leaves that side
+ *            unbounded (-1, -1: no window). causal = 1 sets the right width
+ *            to 0. Section 4.7 names the left boundary of local attention
+ *            without a formula; this is the plainest reading with the
+ *            causal alignment.
  *   pack_gqa 1: the g = Hq / Hkv query heads of one key/value head share a
  *            128-row query tile (rows interleave as query-major, head-minor),
  *            so a K/V tile is read once for the group; 0: one query head per
@@ -209,8 +216,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
                 const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q, int total_k,
-                int causal, float alpha, int dtype, int pack_gqa, int num_splits,
-                float* workspace, int64_t workspace_bytes, void* stream);
+                int causal, int window_left, int window_right, float alpha, int dtype,
+                int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes,
+                void* stream);
 
 /* Workspace bytes attn_fwd_ex needs for num_splits key ranges (0 for
  * num_splits <= 1): num_splits * total_q * Hq * (d + 1) * 4. */

@@ -160,11 +160,12 @@ def _ex(**kw):
     lib = ea.load()
     a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000, lse=FAKE + 0x40000000,
              B=2, Hq=8, Hkv=2, Nq=1, Nk=1000, d=128, cu_q=None, cu_k=None, total_q=0, total_k=0, causal=1,
-             alpha=0.1, dtype=0, pack=-1, splits=1, ws=None, ws_bytes=0, stream=None)
+             wl=-1, wr=-1, alpha=0.1, dtype=0, pack=-1, splits=1, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.attn_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
-                           a["d"], a["cu_q"], a["cu_k"], a["total_q"], a["total_k"], a["causal"], a["alpha"],
-                           a["dtype"], a["pack"], a["splits"], a["ws"], ctypes.c_int64(a["ws_bytes"]), a["stream"])
+                           a["d"], a["cu_q"], a["cu_k"], a["total_q"], a["total_k"], a["causal"], a["wl"], a["wr"],
+                           a["alpha"], a["dtype"], a["pack"], a["splits"], a["ws"], ctypes.c_int64(a["ws_bytes"]),
+                           a["stream"])
 
 
 WS = FAKE + 0x60000000
@@ -189,6 +190,8 @@ WS = FAKE + 0x60000000
      "total_q"),
     (dict(o=FAKE + 0x10000000), ea.ATTN_ERR_INVALID_ARG, "o overlaps k"),
     (dict(Nk=1 << 20, Hkv=8, Hq=8, d=256), ea.ATTN_ERR_UNSUPPORTED, "too long"),
+    (dict(wl=-2), ea.ATTN_ERR_INVALID_ARG, "window"),
+    (dict(wr=-5), ea.ATTN_ERR_INVALID_ARG, "window"),
 ])
 def test_fwd_ex_rejects_bad_arguments_before_launch(kw, status, msg):
     assert _ex(**kw) == status

@@ -31,13 +31,13 @@ def _split_len(nk, s):
     return -(-per // 64) * 64
 
 
-def _dense(ea, B, Nq, Nk, Hq, Hkv, d, causal, pack, splits, seed=0, dtype="bf16", alpha=None):
+def _dense(ea, B, Nq, Nk, Hq, Hkv, d, causal, pack, splits, seed=0, dtype="bf16", alpha=None, window=(-1, -1)):
     import torch
     bits, vals = make_qkv_gqa(B, Nq, Nk, Hq, Hkv, d, seed=seed, dtype=dtype)
     q, k, v = _dev(bits, dtype)
-    o, lse = ea.attention_ex(q, k, v, causal=causal, alpha=alpha, pack_gqa=pack, num_splits=splits)
+    o, lse = ea.attention_ex(q, k, v, causal=causal, alpha=alpha, pack_gqa=pack, num_splits=splits, window=window)
     torch.cuda.synchronize()
-    o_ref, l_ref = attention_gqa(*vals, alpha, causal)
+    o_ref, l_ref = attention_gqa(*vals, alpha, causal, window=window)
     return to_f64(o), to_f64(lse), o_ref, l_ref
 
 
@@ -121,7 +121,7 @@ def test_ex_matches_attn_fwd_bitwise(gpu):
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def _varlen(ea, lens_q, lens_k, Hq, Hkv, d, causal, splits, pack=-1, seed=0):
+def _varlen(ea, lens_q, lens_k, Hq, Hkv, d, causal, splits, pack=-1, seed=0, window=(-1, -1)):
     import torch
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
@@ -130,9 +130,9 @@ def _varlen(ea, lens_q, lens_k, Hq, Hkv, d, causal, splits, pack=-1, seed=0):
     tq, tk = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
     o, lse = ea.attention_ex(q, k, v, causal=causal, cu_seqlens_q=tq, cu_seqlens_k=tk,
                              max_seqlen_q=int(max(lens_q)), max_seqlen_k=int(max(lens_k)), pack_gqa=pack,
-                             num_splits=splits)
+                             num_splits=splits, window=window)
     torch.cuda.synchronize()
-    o_ref, l_ref = attention_varlen(vals[0][0], vals[1][0], vals[2][0], cu_q, cu_k, None, causal)
+    o_ref, l_ref = attention_varlen(vals[0][0], vals[1][0], vals[2][0], cu_q, cu_k, None, causal, window=window)
     return to_f64(o), to_f64(lse), o_ref, l_ref
 
 
@@ -186,3 +186,21 @@ def test_varlen_decode(gpu, splits):
 def test_decode_f16_alpha(gpu):
     o, lse, o_ref, l_ref = _dense(gpu, 3, 1, 3000, 4, 1, 128, False, -1, 4, seed=12, dtype="f16", alpha=0.05)
     _check(o, lse, o_ref, l_ref, "f16")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("window", [(0, 0), (16, 0), (100, 50), (-1, 30), (300, -1), (31, 32)])
+def test_local_window(gpu, d, window):
+    for nq, nk, causal, splits in ((200, 200, False, 1), (77, 300, True, 1), (300, 77, False, 3)):
+        o, lse, o_ref, l_ref = _dense(gpu, 2, nq, nk, 4, 2, d, causal, -1, splits, seed=d + nq, window=window)
+        _check(o, lse, o_ref, l_ref, (d, window, nq, nk, causal, splits))
+
+
+@pytest.mark.parametrize("window", [(256, 0), (0, -1), (1000, 10)])
+def test_local_window_decode_and_varlen(gpu, window):
+    o, lse, o_ref, l_ref = _dense(gpu, 3, 2, 2000, 16, 2, 128, True, -1, 4, seed=13, window=window)
+    _check(o, lse, o_ref, l_ref, ("decode", window))
+    lens_q, _ = make_seqlens(6, 1, 200, seed=4)
+    lens_k, _ = make_seqlens(6, 1, 500, seed=5)
+    o, lse, o_ref, l_ref = _varlen(gpu, lens_q, lens_k, 4, 4, 64, False, 2, seed=9, window=window)
+    _check(o, lse, o_ref, l_ref, ("varlen", window))
