@@ -30,6 +30,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}  # MI355X dense MFM
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 METRIC = "attention fwd TFLOPS + % of MFMA peak, bf16 d=128 N=8k (and fp8)"
 HEADLINE = dict(B=2, N=8192, H=16, d=128, causal=False)
+DECODE = dict(B=8, Hq=64, Hkv=8, Nk=8192, d=128)  # one new token, GQA 8:1, 8192-key cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_d128_n8192.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_forward_attn_amd", "csrc", "attn_fwd.hip")
 
@@ -317,6 +318,8 @@ def main():
     ap.add_argument("--fp8", action="store_true", help="also time the FP8 forward (stderr)")
     ap.add_argument("--bwd", action="store_true", help="also time the backward (stderr)")
     ap.add_argument("--decode", action="store_true", help="also time split-KV decode (stderr)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode workload (8 x 64/8 heads, 8192-key cache) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -341,6 +344,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.decode_only:
+        r = bench_decode(ea, **DECODE, splits=None, steps=args.steps, warmup=args.warmup)
+        print(json.dumps({"decode": r}), flush=True)
+        return
 
     h = HEADLINE
     head = bench_bf16(ea, h["B"], h["N"], h["H"], h["d"], h["causal"], args.steps, args.warmup)
