@@ -320,6 +320,8 @@ def main():
     ap.add_argument("--decode", action="store_true", help="also time split-KV decode (stderr)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode workload (8 x 64/8 heads, 8192-key cache) and exit")
+    ap.add_argument("--bwd-only", action="store_true",
+                    help="time only the backward at the headline shape (causal) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -344,6 +346,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.bwd_only:
+        h = HEADLINE
+        r = bench_bwd(ea, h["B"], h["N"], h["H"], h["d"], True, args.steps, args.warmup)
+        print(json.dumps({"bwd": r}), flush=True)
+        return
 
     if args.decode_only:
         r = bench_decode(ea, **DECODE, splits=None, steps=args.steps, warmup=args.warmup)

@@ -75,6 +75,13 @@ def load():
     if not os.path.exists(lib_path):
         raise RuntimeError(f"{lib_path} is missing: build it with "
                            "`python -m exact_attention_forward_attn_amd.build`")
+    # torch first: the library then binds to the HIP runtime torch has
+    # loaded (opened the other way round, the two can end up on different
+    # runtime instances and launches report no device)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(lib_path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]

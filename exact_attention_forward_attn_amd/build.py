@@ -28,10 +28,13 @@ COMMON = [
 ]
 # packed fp32 VALU forms are kept out of the generated code
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-munsafe-fp-atomics",
-             # MFMA accumulators in VGPRs: the softmax reads every score, and
-             # AGPR-resident scores would need a copy per element
-             "-mllvm", "-amdgpu-mfma-vgpr-form"]
+             "-munsafe-fp-atomics"]
+# MFMA accumulators in VGPRs: the forward's softmax reads every score, and
+# AGPR-resident scores would need a copy per element. The backward keeps its
+# dK/dV accumulators in AGPRs instead (they are read once, at the end), which
+# its one-wave-per-SIMD dK/dV kernel needs for its register budget.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = {"attn_bwd.hip"}
 
 
 def _hipcc():
@@ -59,7 +62,8 @@ def build(verbose: bool = False, out: str = LIB) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             if src.endswith(".hip"):
-                cmd = [hipcc, *HIP_FLAGS, *COMMON, "-c", path, "-o", obj]
+                extra = [] if src in NO_VGPR_FORM else VGPR_FORM
+                cmd = [hipcc, *HIP_FLAGS, *extra, *COMMON, "-c", path, "-o", obj]
             else:
                 cmd = [hipcc, *COMMON, "-x", "c++", "-c", path, "-o", obj]
             jobs.append((cmd, src))

@@ -89,6 +89,10 @@ struct KernelArgs {
 // keeps K, V, dK^T and dV^T in registers
 template <int D>
 constexpr int kWavesDkdv = D == 64 ? 2 : 1;
+// dK/dV kernels that run the software-pipelined loop (those at one wave per
+// SIMD, which have the registers for a second tile's S and dP)
+template <int D>
+constexpr bool kPipeDkdv = D == 128;
 template <int D>
 constexpr int kWavesDq = D == 256 ? 1 : 2;
 
@@ -220,8 +224,10 @@ void dkdv_kernel(KernelArgs a) {
 
   __shared__ __attribute__((aligned(1024))) char qbuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char qbuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char qbuf2[kPipeDkdv<D> ? G::TILE : 16];
   __shared__ __attribute__((aligned(1024))) char obuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf1[G::TILE];
+  __shared__ __attribute__((aligned(1024))) char obuf2[kPipeDkdv<D> ? G::TILE : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -308,41 +314,162 @@ void dkdv_kernel(KernelArgs a) {
   };
 
   f32x4 l2c[4], dlc[4], l2n[4], dln[4];
-  if (t0 < nqt) {
-    copy_tile<D>(to, rq, qbuf0, wave, 32 * t0, RS);
-    copy_tile<D>(to, ro, obuf0, wave, 32 * t0, RS);
-    load_rows(32 * t0, l2c, dlc);
-    wait_vmcnt<0>();
-    barrier_all();
-  }
-  // slot of tile t is (t - t0) % 2; the loop is unrolled by two so that both
-  // slots are compile-time objects
-  auto step = [&](int t, auto j_tag) ATTN_INLINE {
-    constexpr int J = decltype(j_tag)::value;
-    char* qcur = J ? qbuf1 : qbuf0;
-    char* ocur = J ? obuf1 : obuf0;
-    char* qnxt = J ? qbuf0 : qbuf1;
-    char* onxt = J ? obuf0 : obuf1;
-    if (t + 1 < nqt) {
-      copy_tile<D>(to, rq, qnxt, wave, 32 * (t + 1), RS);
-      copy_tile<D>(to, ro, onxt, wave, 32 * (t + 1), RS);
-      load_rows(32 * (t + 1), l2n, dln);
+  if constexpr (!kPipeDkdv<D>) {
+    f32x4 l2c[4], dlc[4], l2n[4], dln[4];
+    if (t0 < nqt) {
+      copy_tile<D>(to, rq, qbuf0, wave, 32 * t0, RS);
+      copy_tile<D>(to, ro, obuf0, wave, 32 * t0, RS);
+      load_rows(32 * t0, l2c, dlc);
+      wait_vmcnt<0>();
+      barrier_all();
     }
-    compute(qcur, ocur, 32 * t, l2c, dlc);
-    wait_vmcnt<0>();
-    barrier_all();
+    // slot of tile t is (t - t0) % 2; the loop is unrolled by two so that both
+    // slots are compile-time objects
+    auto step = [&](int t, auto j_tag) ATTN_INLINE {
+      constexpr int J = decltype(j_tag)::value;
+      char* qcur = J ? qbuf1 : qbuf0;
+      char* ocur = J ? obuf1 : obuf0;
+      char* qnxt = J ? qbuf0 : qbuf1;
+      char* onxt = J ? obuf0 : obuf1;
+      if (t + 1 < nqt) {
+        copy_tile<D>(to, rq, qnxt, wave, 32 * (t + 1), RS);
+        copy_tile<D>(to, ro, onxt, wave, 32 * (t + 1), RS);
+        load_rows(32 * (t + 1), l2n, dln);
+      }
+      compute(qcur, ocur, 32 * t, l2c, dlc);
+      wait_vmcnt<0>();
+      barrier_all();
+  #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l2c[g] = l2n[g];
+        dlc[g] = dln[g];
+      }
+    };
+    int t = t0;
+    for (; t + 1 < nqt; t += 2) {
+      step(t, Int<0>{});
+      step(t + 1, Int<1>{});
+    }
+    if (t < nqt) step(t, Int<0>{});
+
+
+  } else {
+    // Software pipeline (one wave per SIMD, so no other wave fills the
+    // gaps): step t runs the S and dP products of tile t+1 interleaved with
+    // the VALU work of tile t (p and dS), then the dV and dK products of tile
+    // t. Q/dO tiles rotate through three LDS slots: step t reads tiles t
+    // (transposed) and t+1 (rows) while tile t+2 is copied in.
+    f32x16 sc = f32x16{}, dpc = f32x16{};
+    auto slot_q = [&](auto j) ATTN_INLINE -> char* {
+      constexpr int J = decltype(j)::value % 3;
+      return J == 0 ? qbuf0 : J == 1 ? qbuf1 : qbuf2;
+    };
+    auto slot_o = [&](auto j) ATTN_INLINE -> char* {
+      constexpr int J = decltype(j)::value % 3;
+      return J == 0 ? obuf0 : J == 1 ? obuf1 : obuf2;
+    };
+    if (t0 < nqt) {
+      copy_tile<D>(to, rq, qbuf0, wave, 32 * t0, RS);
+      copy_tile<D>(to, ro, obuf0, wave, 32 * t0, RS);
+      if (t0 + 1 < nqt) {
+        copy_tile<D>(to, rq, qbuf1, wave, 32 * (t0 + 1), RS);
+        copy_tile<D>(to, ro, obuf1, wave, 32 * (t0 + 1), RS);
+      }
+      load_rows(32 * t0, l2c, dlc);
+      wait_vmcnt<0>();
+      barrier_all();
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      l2c[g] = l2n[g];
-      dlc[g] = dln[g];
+      for (int kc = 0; kc < KC; ++kc) sc = E::mfma(row_op<D, T>(to, qbuf0, kc), kreg[kc], sc);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) dpc = E::mfma(row_op<D, T>(to, obuf0, kc), vreg[kc], dpc);
     }
-  };
-  int t = t0;
-  for (; t + 1 < nqt; t += 2) {
-    step(t, Int<0>{});
-    step(t + 1, Int<1>{});
+    constexpr int NM = 2 * KC;  // S and dP MFMAs of one tile
+    auto pstep = [&](int t, auto j_tag, auto next_tag) ATTN_INLINE {
+      constexpr int J = decltype(j_tag)::value;
+      constexpr bool NEXT = decltype(next_tag)::value;  // tile t+1 exists
+      const char* qn = slot_q(Int<J + 1>{});
+      const char* on = slot_o(Int<J + 1>{});
+      if (t + 2 < nqt) {
+        copy_tile<D>(to, rq, slot_q(Int<J + 2>{}), wave, 32 * (t + 2), RS);
+        copy_tile<D>(to, ro, slot_o(Int<J + 2>{}), wave, 32 * (t + 2), RS);
+      }
+      if (NEXT) load_rows(32 * (t + 1), l2n, dln);
+      f32x16 sn = f32x16{}, dpn = f32x16{};
+      float pv[16], dsv[16];
+      const int q0t = 32 * t;
+      // operand ring: the LDS read of MFMA m + 2 is issued at step m
+      v8 ring[2];
+      auto opnd = [&](auto m_tag) ATTN_INLINE -> v8 {
+        constexpr int m = decltype(m_tag)::value;
+        return m < KC ? row_op<D, T>(to, qn, m) : row_op<D, T>(to, on, m - KC);
+      };
+      if constexpr (NEXT) {
+        ring[0] = opnd(Int<0>{});
+        ring[1] = opnd(Int<1>{});
+      }
+      For<0, NM>::run([&](auto m_tag) ATTN_INLINE {
+        constexpr int m = decltype(m_tag)::value;
+        if constexpr (NEXT) {
+          if constexpr (m < KC)
+            sn = E::mfma(ring[m % 2], kreg[m], sn);
+          else
+            dpn = E::mfma(ring[m % 2], vreg[m - KC], dpn);
+          if constexpr (m + 2 < NM) ring[m % 2] = opnd(Int<m + 2>{});
+        }
+        // p and dS of the scores assigned to this step
+        For<(m * 16) / NM, ((m + 1) * 16) / NM>::run([&](auto r_tag) ATTN_INLINE {
+          constexpr int r = decltype(r_tag)::value;
+          const int qr = q0t + 8 * (r >> 2) + 4 * h32 + (r & 3);
+          const bool ok = qr < N && key < N && (!CAUSAL || key <= qr);
+          const float lse = l2c[r >> 2][r & 3];
+          const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(sc[r], c, -lse * kLog2e)) : 0.f;
+          pv[r] = p;
+          dsv[r] = p * (dpc[r] - dlc[r >> 2][r & 3]);
+          pin(dsv[r]);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      v8 pk[2], dk8[2];
+      pack16<T>(pv, pk);
+      pack16<T>(dsv, dk8);
+      const char* qc = slot_q(Int<J>{});
+      const char* oc = slot_o(Int<J>{});
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dvt[db] = E::mfma(tr_op<D, T>(to, oc, db, ks), pk[ks], dvt[db]);
+          dkt[db] = E::mfma(tr_op<D, T>(to, qc, db, ks), dk8[ks], dkt[db]);
+        }
+      wait_vmcnt<0>();
+      barrier_all();
+      sc = sn;
+      dpc = dpn;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        l2c[g] = l2n[g];
+        dlc[g] = dln[g];
+      }
+    };
+    // unrolled by three so every slot is a compile-time object
+    int t = t0;
+    for (; t + 3 < nqt; t += 3) {
+      pstep(t, Int<0>{}, TrueT{});
+      pstep(t + 1, Int<1>{}, TrueT{});
+      pstep(t + 2, Int<2>{}, TrueT{});
+    }
+    // 0 to 3 tiles left (the last one without a next tile)
+    if (t + 2 < nqt) {
+      pstep(t, Int<0>{}, TrueT{});
+      pstep(t + 1, Int<1>{}, TrueT{});
+      pstep(t + 2, Int<2>{}, FalseT{});
+    } else if (t + 1 < nqt) {
+      pstep(t, Int<0>{}, TrueT{});
+      pstep(t + 1, Int<1>{}, FalseT{});
+    } else if (t < nqt) {
+      pstep(t, Int<0>{}, FalseT{});
+    }
   }
-  if (t < nqt) step(t, Int<0>{});
 
   if (key < N) {
     store_rows<D, T>((T*)a.dk + head_off, key, (uint32_t)a.H * D, h32, dkt, a.alpha);
