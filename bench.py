@@ -377,7 +377,7 @@ def main():
         extra["sweep"] = rows
     if args.bwd:
         rows = []
-        for d, H in ((64, 32), (128, 16)):
+        for d, H in ((64, 32), (128, 16), (256, 8)):
             for N in (1024, 4096, 8192):
                 for causal in (False, True):
                     r = bench_bwd(ea, 16384 // N, N, H, d, causal, max(5, args.steps // 4), 2)

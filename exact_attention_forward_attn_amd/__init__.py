@@ -18,7 +18,7 @@ Functions (same names as the C ABI):
 alpha=None, block_rows=128, stream=None)``
     Forward on e4m3 inputs with a bf16 output.
 ``attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None)``
-    16-bit backward (d = 64 or 128): gradients dq, dk, dv of the forward's
+    16-bit backward (d = 64, 128 or 256): gradients dq, dk, dv of the forward's
     O = softmax(alpha q k^T) v for an upstream gradient dout; o and lse are
     the forward's outputs; delta is a float32 [B, H, N] workspace the call
     fills with rowsum(dout * o).

@@ -276,7 +276,6 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   const int s = check_shape(B, H, N, d, 2);
   if (s == 1) return ok();
   if (s != ATTN_OK) return s;
-  if (d == 256) return fail(ATTN_ERR_UNSUPPORTED, "attn_bwd supports d = 64 and 128 (got 256)");
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (!std::isfinite(alpha) || alpha < 0.f)
     return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);

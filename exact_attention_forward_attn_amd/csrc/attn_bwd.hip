@@ -211,10 +211,16 @@ __device__ __forceinline__ void pack16(const float (&x)[16], typename Elt<T>::v8
 }
 
 // ---- dK, dV: KV-parallel ---------------------------------------------------------
-template <int D, bool CAUSAL, typename T>
+// PARTS selects the outputs: 3 = dK and dV in one pass; at d = 256 their
+// accumulators, K and V do not fit one wave's registers, so the kernel runs
+// twice, 1 = dV (needs K for S), then 2 = dK (needs K and V), recomputing S.
+template <int D, bool CAUSAL, typename T, int PARTS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesDkdv<D>, kWavesDkdv<D>)))
 void dkdv_kernel(KernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool DO_K = (PARTS & 2) != 0;
+  constexpr bool DO_V = (PARTS & 1) != 0;
+  constexpr bool PIPE = kPipeDkdv<D> && PARTS == 3;
   typedef Elt<T> E;
   typedef typename E::v8 v8;
   typedef Geo<D, 1> G;
@@ -224,10 +230,10 @@ void dkdv_kernel(KernelArgs a) {
 
   __shared__ __attribute__((aligned(1024))) char qbuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char qbuf1[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char qbuf2[kPipeDkdv<D> ? G::TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char qbuf2[PIPE ? G::TILE : 16];
   __shared__ __attribute__((aligned(1024))) char obuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf1[G::TILE];
-  __shared__ __attribute__((aligned(1024))) char obuf2[kPipeDkdv<D> ? G::TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char obuf2[PIPE ? G::TILE : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -253,17 +259,17 @@ void dkdv_kernel(KernelArgs a) {
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (int64_t)bh * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (int64_t)bh * N, (uint32_t)N * 4);
 
-  v8 kreg[KC], vreg[KC];
+  v8 kreg[KC], vreg[DO_K ? KC : 1];
   load_row_operand<D, T>(rk, (uint32_t)key, RS, h32, kreg);
-  load_row_operand<D, T>(rv, (uint32_t)key, RS, h32, vreg);
+  if constexpr (DO_K) load_row_operand<D, T>(rv, (uint32_t)key, RS, h32, vreg);
   TO to;
   to.init(lane, wave, RS);
 
-  f32x16 dkt[DB], dvt[DB];
+  f32x16 dkt[DO_K ? DB : 1], dvt[DO_V ? DB : 1];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    dkt[db] = f32x16{};
-    dvt[db] = f32x16{};
+    if constexpr (DO_K) dkt[db] = f32x16{};
+    if constexpr (DO_V) dvt[db] = f32x16{};
   }
   const float c = a.c;
 
@@ -288,8 +294,10 @@ void dkdv_kernel(KernelArgs a) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) s = E::mfma(row_op<D, T>(to, qt, kc), kreg[kc], s);
+    if constexpr (DO_K) {
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) dp = E::mfma(row_op<D, T>(to, ot, kc), vreg[kc], dp);
+      for (int kc = 0; kc < KC; ++kc) dp = E::mfma(row_op<D, T>(to, ot, kc), vreg[kc], dp);
+    }
     float pv[16], dsv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -299,22 +307,22 @@ void dkdv_kernel(KernelArgs a) {
       // a row with LSE = -inf has no keys; its p stays 0
       const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(s[r], c, -lse * kLog2e)) : 0.f;
       pv[r] = p;
-      dsv[r] = p * (dp[r] - dl[r >> 2][r & 3]);
+      if constexpr (DO_K) dsv[r] = p * (dp[r] - dl[r >> 2][r & 3]);
     }
     v8 pk[2], dk8[2];
-    pack16<T>(pv, pk);
-    pack16<T>(dsv, dk8);
+    if constexpr (DO_V) pack16<T>(pv, pk);
+    if constexpr (DO_K) pack16<T>(dsv, dk8);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dvt[db] = E::mfma(tr_op<D, T>(to, ot, db, ks), pk[ks], dvt[db]);
-        dkt[db] = E::mfma(tr_op<D, T>(to, qt, db, ks), dk8[ks], dkt[db]);
+        if constexpr (DO_V) dvt[db] = E::mfma(tr_op<D, T>(to, ot, db, ks), pk[ks], dvt[db]);
+        if constexpr (DO_K) dkt[db] = E::mfma(tr_op<D, T>(to, qt, db, ks), dk8[ks], dkt[db]);
       }
   };
 
   f32x4 l2c[4], dlc[4], l2n[4], dln[4];
-  if constexpr (!kPipeDkdv<D>) {
+  if constexpr (!PIPE) {
     f32x4 l2c[4], dlc[4], l2n[4], dln[4];
     if (t0 < nqt) {
       copy_tile<D>(to, rq, qbuf0, wave, 32 * t0, RS);
@@ -472,8 +480,8 @@ void dkdv_kernel(KernelArgs a) {
   }
 
   if (key < N) {
-    store_rows<D, T>((T*)a.dk + head_off, key, (uint32_t)a.H * D, h32, dkt, a.alpha);
-    store_rows<D, T>((T*)a.dv + head_off, key, (uint32_t)a.H * D, h32, dvt, 1.0f);
+    if constexpr (DO_K) store_rows<D, T>((T*)a.dk + head_off, key, (uint32_t)a.H * D, h32, dkt, a.alpha);
+    if constexpr (DO_V) store_rows<D, T>((T*)a.dv + head_off, key, (uint32_t)a.H * D, h32, dvt, 1.0f);
   }
 #endif
 }
@@ -603,10 +611,20 @@ int launch_d(const BwdArgs& f, hipStream_t st) {
   a.alpha = f.alpha;
   const int grid = a.n_blk * f.B * f.H;
   if (f.causal) {
-    hipLaunchKernelGGL((dkdv_kernel<D, true, T>), dim3(grid), dim3(256), 0, st, a);
+    if constexpr (D == 256) {
+      hipLaunchKernelGGL((dkdv_kernel<D, true, T, 1>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((dkdv_kernel<D, true, T, 2>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, true, T, 3>), dim3(grid), dim3(256), 0, st, a);
+    }
     hipLaunchKernelGGL((dq_kernel<D, true, T>), dim3(grid), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<D, false, T>), dim3(grid), dim3(256), 0, st, a);
+    if constexpr (D == 256) {
+      hipLaunchKernelGGL((dkdv_kernel<D, false, T, 1>), dim3(grid), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((dkdv_kernel<D, false, T, 2>), dim3(grid), dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, false, T, 3>), dim3(grid), dim3(256), 0, st, a);
+    }
     hipLaunchKernelGGL((dq_kernel<D, false, T>), dim3(grid), dim3(256), 0, st, a);
   }
   return (int)hipGetLastError();
@@ -617,6 +635,7 @@ int dispatch(const BwdArgs& f, hipStream_t st) {
   switch (f.d) {
     case 64: return launch_d<64, T>(f, st);
     case 128: return launch_d<128, T>(f, st);
+    case 256: return launch_d<256, T>(f, st);
   }
   return (int)hipErrorInvalidValue;
 }

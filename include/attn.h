@@ -146,7 +146,9 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
  *   dq, dk, dv  [B, N, H, d] outputs in the input dtype (device memory).
  *   delta    [B, H, N] float32 workspace owned by the caller; the call writes
  *            D into it (no allocation inside the library).
- *   d        64 or 128 (d = 256 returns ATTN_ERR_UNSUPPORTED).
+ *   d        64, 128 or 256 (at 256 the dK/dV kernel runs twice, once per
+ *            output, recomputing S, because one wave cannot hold K, V and both
+ *            accumulators).
  *   Other arguments and the error behaviour as attn_fwd. dq, dk, dv and delta
  *   must not overlap each other or the inputs.
  *

@@ -53,7 +53,7 @@ def _check(grads, vals, do_vals, causal, alpha=None, tag=""):
         assert e["rel_max"] <= REL_MAX and e["rel_rms"] <= REL_RMS, (tag, name, e)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 33, 129, 300])
 def test_bwd_small_shapes(gpu, d, causal, N):
@@ -93,3 +93,10 @@ def test_bwd_is_deterministic(gpu):
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_head_dim_256_several_tiles(gpu, causal):
+    # d = 256 runs the dK/dV kernel twice (dV, then dK)
+    grads, vals, do_vals, _ = _run(gpu, 1, 700, 2, 256, causal, seed=13)
+    _check(grads, vals, do_vals, causal, tag=("d256", causal))
