@@ -24,12 +24,14 @@ import numpy as np
 
 from .attention import causal_mask
 
-__all__ = ["attention_backward", "attention_backward_head"]
+__all__ = ["attention_backward", "attention_backward_head", "attention_backward_gqa"]
 
 
 def attention_backward_head(q, k, v, do, alpha, causal=False, row_chunk=1024):
-    """Gradients (dq, dk, dv) of one head: q, k, v, do are (N, d) float64."""
+    """Gradients (dq, dk, dv) of one head: q, do are (N_q, d), k, v are
+    (N_k, d) float64; causal uses the bottom-right alignment of the forward."""
     n = q.shape[0]
+    nk = k.shape[0]
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -37,7 +39,7 @@ def attention_backward_head(q, k, v, do, alpha, causal=False, row_chunk=1024):
         r1 = min(n, r0 + row_chunk)
         s = alpha * (q[r0:r1] @ k.T)
         if causal:
-            s = np.where(causal_mask(n, n)[r0:r1], -np.inf, s)
+            s = np.where(causal_mask(n, nk)[r0:r1], -np.inf, s)
         m = s.max(axis=1, keepdims=True)
         live = np.isfinite(m)
         e = np.where(live, np.exp(s - np.where(live, m, 0.0)), 0.0)
@@ -72,4 +74,37 @@ def attention_backward(q, k, v, do, alpha=None, causal=False, row_chunk=1024):
             dq[b, :, h, :] = gq
             dk[b, :, h, :] = gk
             dv[b, :, h, :] = gv
+    return dq, dk, dv
+
+
+def attention_backward_gqa(q, k, v, do, alpha=None, causal=False):
+    """Gradients for H_q query heads over H_kv key/value heads.
+
+    q, do are (B, N_q, H_q, d); k, v are (B, N_k, H_kv, d). Query head h
+    reads key/value head floor(h / g) ("FlashAttention-3 on Hopper",
+    section 5.6.1), so by the chain rule the gradient of a key/value head is
+    the sum of the per-head gradients of the g query heads that read it
+    (section 8.8 describes that accumulation).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, nq, hq, d = q.shape
+    hkv = k.shape[2]
+    if hkv < 1 or hq % hkv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    g = hq // hkv
+    if alpha is None:
+        alpha = 1.0 / np.sqrt(d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(hq):
+            kh = h // g
+            gq, gk, gv = attention_backward_head(q[b, :, h], k[b, :, kh], v[b, :, kh], do[b, :, h], alpha, causal)
+            dq[b, :, h] = gq
+            dk[b, :, kh] += gk
+            dv[b, :, kh] += gv
     return dq, dk, dv

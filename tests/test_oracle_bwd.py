@@ -104,3 +104,45 @@ def test_backward_causal_first_row_and_row_chunks():
     g1 = attention_backward(q, k, v, do, 0.3, True, row_chunk=7)
     for a, b in zip((dq, dk, dv), g1):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(3, 6), (6, 3)])
+def test_gqa_backward_matches_central_differences(causal, nq, nk):
+    # 4 query heads over 2 KV heads, N_q != N_k (bottom-right causal): the
+    # gradients of sum(O o dO), O from the GQA forward oracle, by differences
+    from oracle.attention_bwd import attention_backward_gqa
+    from oracle.variants import attention_gqa
+    B, hq, hkv, d = 1, 4, 2, 3
+    q, do = _rand((B, nq, hq, d), 50), _rand((B, nq, hq, d), 51)
+    k, v = _rand((B, nk, hkv, d), 52), _rand((B, nk, hkv, d), 53)
+    alpha = 0.6
+    dq, dk, dv = attention_backward_gqa(q, k, v, do, alpha, causal)
+
+    def loss(q_, k_, v_):
+        o, _ = attention_gqa(q_, k_, v_, alpha, causal)
+        return float(np.sum(o * do))
+    eps = 1e-6
+    for name, x, gr in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"])
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(gr, fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_gqa_backward_with_one_group_is_mha():
+    from oracle.attention_bwd import attention_backward_gqa
+    B, N, H, d = 2, 9, 3, 4
+    q, k, v, do = (_rand((B, N, H, d), 60 + s) for s in range(4))
+    for causal in (False, True):
+        a = attention_backward_gqa(q, k, v, do, 0.5, causal)
+        b = attention_backward(q, k, v, do, 0.5, causal)
+        for x, y in zip(a, b):
+            np.testing.assert_allclose(x, y, rtol=1e-14, atol=1e-15)
