@@ -31,6 +31,8 @@ max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, workspace=None,
 ``attn_splitkv_workspace_bytes``, ``attn_pack_gqa_heuristic``,
 ``attn_num_splits_heuristic``
     Sizing helpers of attn_fwd_ex (pure host functions).
+``attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None)``
+    Backward with Hq query heads over Hkv key/value heads and N_q != N_k.
 ``attn_last_error()``
     Message of the last failed call on this thread.
 
@@ -44,7 +46,8 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_fwd_ex",
+    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_bwd_ex",
+    "attention_backward_ex", "attn_fwd_ex",
     "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
     "attn_last_error", "attention", "attention_ex", "attention_backward", "fp8_prepare", "attention_fp8",
     "EXPORTED_SYMBOLS",
@@ -56,7 +59,7 @@ _lib = None
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 DTYPE_BF16, DTYPE_F16 = 0, 1
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_fwd_ex",
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_bwd_ex", "attn_fwd_ex",
                     "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
                     "attn_last_error", "attn_version")
 
@@ -92,6 +95,8 @@ def load():
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_bwd.restype = i
+    lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.attn_bwd_ex.restype = i
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, i, i, f, i, i, i, vp,
                                 ctypes.c_int64, vp]
     lib.attn_fwd_ex.restype = i
@@ -309,6 +314,40 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None,
                         _ptr(delta), B, H, N, d, int(bool(causal)), _default_alpha(d, alpha), dt,
                         _stream_handle(stream)))
     return dq, dk, dv
+
+
+def attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None):
+    """Backward with Hq query heads over Hkv key/value heads and N_q != N_k:
+    q, o, dout, dq [B, Nq, Hq, d]; k, v, dk, dv [B, Nk, Hkv, d]; lse and
+    delta float32 [B, Hq, Nq]."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Nq, Hq, d] and k [B, Nk, Hkv, d]")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    for t, n in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
+        _require(t, n, q.dtype, q.shape, q.device)
+    for t, n in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _require(t, n, q.dtype, k.shape, q.device)
+    _require(lse, "lse", torch.float32, (B, Hq, Nq), q.device)
+    _require(delta, "delta", torch.float32, (B, Hq, Nq), q.device)
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    _check(lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(delta), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), _default_alpha(d, alpha), dt,
+                           _stream_handle(stream)))
+    return dq, dk, dv
+
+
+def attention_backward_ex(q, k, v, o, lse, dout, causal=False, alpha=None, stream=None):
+    """Allocate dq, dk, dv and the workspace with torch and run attn_bwd_ex."""
+    torch = _torch()
+    B, Nq, Hq, d = q.shape
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    return attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal, alpha, stream)
 
 
 def attention_backward(q, k, v, o, lse, dout, causal=False, alpha=None, stream=None):

@@ -297,11 +297,59 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
   a.B = B; a.H = H; a.N = N; a.d = d;
+  a.Hkv = H; a.Nk = N;
   a.causal = causal;
   a.dtype = dtype;
   a.scale_log2 = scale_log2(alpha);
   a.alpha = a.scale_log2 / 1.4426950408889634f;
   return hip_status(attn::launch_bwd_16(a, stream), "attn_bwd launch");
+}
+
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                int causal, float alpha, int dtype, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
+    return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
+    return fail(ATTN_ERR_INVALID_ARG, "B, Hq, Hkv, Nq, Nk must be >= 0 (got %d, %d, %d, %d, %d)", B, Hq, Hkv,
+                Nq, Nk);
+  if (d != 64 && d != 128 && d != 256)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension d=%d is not supported (64, 128 or 256)", d);
+  if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0))
+    return fail(ATTN_ERR_INVALID_ARG, "Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!std::isfinite(alpha) || alpha < 0.f)
+    return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
+  if (B == 0 || Hq == 0 || (Nq == 0 && Nk == 0)) return ok();
+  if (((int64_t)Nq + 128) * Hq * d * 2 >= (int64_t(1) << 31) || ((int64_t)Nk + 128) * Hkv * d * 2 >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "sequence too long for the number of heads (N*H*d*2 near 2^31)");
+  if ((int64_t)B * Hq * Nq >= (int64_t(1) << 31) || (int64_t)B * Hkv * Nk >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "B*H*N too large (>= 2^31)");
+  const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
+  const char* names[10] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta"};
+  const int64_t qb = (int64_t)B * Nq * Hq * d * 2, kb = (int64_t)B * Nk * Hkv * d * 2;
+  const int64_t rb = (int64_t)B * Hq * Nq * 4;
+  const int64_t bytes[10] = {qb, kb, kb, qb, qb, rb, qb, kb, kb, rb};
+  // operands of size zero (Nq = 0 or Nk = 0) may be null
+  for (int i = 0; i < 10; ++i) {
+    if (bytes[i] == 0) continue;
+    if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
+  for (int i = 6; i < 10; ++i)
+    for (int j = 0; j < 10; ++j)
+      if (j != i && overlaps(ptrs[i], bytes[i], ptrs[j], bytes[j]))
+        return fail(ATTN_ERR_INVALID_ARG, "%s overlaps %s", names[i], names[j]);
+  attn::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.B = B; a.H = Hq; a.N = Nq; a.d = d;
+  a.Hkv = Hkv; a.Nk = Nk;
+  a.causal = causal;
+  a.dtype = dtype;
+  a.scale_log2 = scale_log2(alpha);
+  a.alpha = a.scale_log2 / 1.4426950408889634f;
+  return hip_status(attn::launch_bwd_16(a, stream), "attn_bwd_ex launch");
 }
 
 int attn_fp8_prepare(const void* x, void* x8, float* descale, int B, int H, int N, int d, int block_rows,

@@ -79,9 +79,11 @@ struct KernelArgs {
   void* dq;
   void* dk;
   void* dv;
-  int B, H, N;
-  int n_blk;      // ceil(N / 128)
-  float c;        // alpha * log2(e)
+  int B, Hq, Hkv, g;  // query heads, key/value heads, g = Hq / Hkv
+  int Nq, Nk;         // query and key rows per batch entry
+  int n_kblk;         // ceil(Nk / 128): dK/dV workgroups per (b, KV head)
+  int n_qblk;         // ceil(Nq / 128): dQ workgroups per (b, query head)
+  float c;            // alpha * log2(e)
   float alpha;
 };
 
@@ -133,12 +135,14 @@ struct TileOffsets {
   }
 };
 
-// Copy 32 rows starting at row0 of one head into an LDS tile (K-style swizzle).
+// Copy 32 rows starting at row0 of one head into an LDS tile (K-style
+// swizzle); extra is a byte offset added to every row (the head within a
+// group of heads that share the buffer resource).
 template <int D>
 __device__ __forceinline__ void copy_tile(const TileOffsets<D>& to, const __amdgpu_buffer_rsrc_t& rs, char* dst,
-                                          int wave, int row0, uint32_t RS) {
+                                          int wave, int row0, uint32_t RS, uint32_t extra = 0) {
   typedef Geo<D, 1> G;
-  const uint32_t base = (uint32_t)row0 * RS;
+  const uint32_t base = (uint32_t)row0 * RS + extra;
 #pragma unroll
   for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
     const uint32_t voff = to.cg[(t & 1) % TileOffsets<D>::KGP] + (base + (uint32_t)t * 4 * G::RPS * RS);
@@ -239,31 +243,39 @@ void dkdv_kernel(KernelArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
 
-  // key blocks: causal grids go from the first block (the longest query
-  // range) to the last
-  const int BH = a.B * a.H;
+  // key blocks of one key/value head: causal grids go from the first block
+  // (the longest query range) to the last. With grouped heads the g query
+  // heads that read this key/value head all contribute to its dK and dV
+  // ("FlashAttention-3 on Hopper", section 8.8); the workgroup loops over
+  // their query tiles itself, so the sum needs no atomics.
+  const int BH = a.B * a.Hkv;
   int kblk, bh;
-  decode_block(blockIdx.x, a.n_blk, BH, CAUSAL, kblk, bh);
-  if (CAUSAL) kblk = a.n_blk - 1 - kblk;
-  const int b = bh / a.H, hh = bh % a.H;
-  const int N = a.N;
+  decode_block(blockIdx.x, a.n_kblk, BH, CAUSAL, kblk, bh);
+  if (CAUSAL) kblk = a.n_kblk - 1 - kblk;
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int Nq = a.Nq, Nk = a.Nk, grp = a.g;
+  const int off = Nk - Nq;                // causal offset (bottom-right)
   const int k0 = kblk * 128;
   const int key = k0 + 32 * wave + l32;   // this lane's key (column of S)
-  const uint32_t RS = (uint32_t)a.H * D * 2;
-  const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;
-  const uint32_t span = (uint32_t)(N - 1) * RS + D * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + head_off, span);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + head_off, span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + head_off, span);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.dout + head_off, span);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (int64_t)bh * N, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (int64_t)bh * N, (uint32_t)N * 4);
+  const uint32_t RSQ = (uint32_t)a.Hq * D * 2, RSK = (uint32_t)a.Hkv * D * 2;
+  const int64_t k_off = ((int64_t)b * Nk * a.Hkv + hk) * D;
+  const int64_t q_off = ((int64_t)b * Nq * a.Hq + (int64_t)hk * grp) * D;  // first head of the group
+  const uint32_t kspan = (uint32_t)(Nk - 1) * RSK + D * 2;
+  const uint32_t qspan = Nq > 0 ? (uint32_t)(Nq - 1) * RSQ + (uint32_t)grp * D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + q_off, qspan);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + k_off, kspan);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + k_off, kspan);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.dout + q_off, qspan);
+  // LSE and D of the group's heads: [g][Nq] from (b, first head)
+  const int64_t l_off = ((int64_t)b * a.Hq + (int64_t)hk * grp) * Nq;
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + l_off, (uint32_t)grp * Nq * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + l_off, (uint32_t)grp * Nq * 4);
 
   v8 kreg[KC], vreg[DO_K ? KC : 1];
-  load_row_operand<D, T>(rk, (uint32_t)key, RS, h32, kreg);
-  if constexpr (DO_K) load_row_operand<D, T>(rv, (uint32_t)key, RS, h32, vreg);
+  load_row_operand<D, T>(rk, (uint32_t)key, RSK, h32, kreg);
+  if constexpr (DO_K) load_row_operand<D, T>(rv, (uint32_t)key, RSK, h32, vreg);
   TO to;
-  to.init(lane, wave, RS);
+  to.init(lane, wave, RSQ);
 
   f32x16 dkt[DO_K ? DB : 1], dvt[DO_V ? DB : 1];
 #pragma unroll
@@ -273,22 +285,32 @@ void dkdv_kernel(KernelArgs a) {
   }
   const float c = a.c;
 
-  // LSE and D of the 16 query rows a lane holds in a tile: rows 8g + 4*h32 +
-  // 0..3 of the tile for g = 0..3 (dword loads: rows past N read as 0 one by
-  // one, and those rows are masked anyway)
-  auto load_rows = [&](int q0t, f32x4 (&l2)[4], f32x4 (&dl)[4]) ATTN_INLINE {
+  // LSE and D of the 16 query rows a lane holds in a tile of head j of the
+  // group: rows 8g + 4*h32 + 0..3 of the tile for g = 0..3 (dword loads;
+  // rows past Nq are masked, and past the group's end read as 0)
+  auto load_rows = [&](int q0t, int j, f32x4 (&l2)[4], f32x4 (&dl)[4]) ATTN_INLINE {
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t off = (uint32_t)(q0t + 8 * g + 4 * h32 + e) * 4;
-        l2[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0));
-        dl[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, off, 0, 0));
+        const int row = q0t + 8 * g + 4 * h32 + e;
+        const uint32_t lo = row < Nq ? ((uint32_t)j * Nq + row) * 4 : 0xffffffffu;
+        l2[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0));
+        dl[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lo, 0, 0));
       }
   };
 
-  const int nqt = (N + 31) / 32;
-  const int t0 = CAUSAL ? k0 / 32 : 0;   // query rows below k0 meet none of these keys
+  // query tiles of one head: query n sees key k iff k <= n + off, so rows
+  // below k0 - off meet none of these keys; the loop runs over
+  // (head of the group, tile) pairs u = j * nt_h + (t - t0)
+  const int nqt = (Nq + 31) / 32;
+  const int t0 = CAUSAL ? min(nqt, max(0, k0 - off) / 32) : 0;
+  const int nt_h = nqt - t0;
+  const int nu = grp * nt_h;
+  auto tile_of = [&](int u, int& q0t, int& j) ATTN_INLINE {
+    j = u / nt_h;
+    q0t = 32 * (t0 + u - j * nt_h);
+  };
 
   auto compute = [&](const char* qt, const char* ot, int q0t, const f32x4 (&l2)[4], const f32x4 (&dl)[4]) ATTN_INLINE {
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -302,7 +324,7 @@ void dkdv_kernel(KernelArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qr = q0t + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      const bool ok = qr < N && key < N && (!CAUSAL || key <= qr);
+      const bool ok = qr < Nq && key < Nk && (!CAUSAL || key <= qr + off);
       const float lse = l2[r >> 2][r & 3];
       // a row with LSE = -inf has no keys; its p stays 0
       const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(s[r], c, -lse * kLog2e)) : 0.f;
@@ -321,52 +343,56 @@ void dkdv_kernel(KernelArgs a) {
       }
   };
 
-  f32x4 l2c[4], dlc[4], l2n[4], dln[4];
   if constexpr (!PIPE) {
     f32x4 l2c[4], dlc[4], l2n[4], dln[4];
-    if (t0 < nqt) {
-      copy_tile<D>(to, rq, qbuf0, wave, 32 * t0, RS);
-      copy_tile<D>(to, ro, obuf0, wave, 32 * t0, RS);
-      load_rows(32 * t0, l2c, dlc);
+    if (nu > 0) {
+      int q0t, j;
+      tile_of(0, q0t, j);
+      copy_tile<D>(to, rq, qbuf0, wave, q0t, RSQ, (uint32_t)j * D * 2);
+      copy_tile<D>(to, ro, obuf0, wave, q0t, RSQ, (uint32_t)j * D * 2);
+      load_rows(q0t, j, l2c, dlc);
       wait_vmcnt<0>();
       barrier_all();
     }
-    // slot of tile t is (t - t0) % 2; the loop is unrolled by two so that both
+    // slot of tile u is u % 2; the loop is unrolled by two so that both
     // slots are compile-time objects
-    auto step = [&](int t, auto j_tag) ATTN_INLINE {
+    auto step = [&](int u, auto j_tag) ATTN_INLINE {
       constexpr int J = decltype(j_tag)::value;
       char* qcur = J ? qbuf1 : qbuf0;
       char* ocur = J ? obuf1 : obuf0;
       char* qnxt = J ? qbuf0 : qbuf1;
       char* onxt = J ? obuf0 : obuf1;
-      if (t + 1 < nqt) {
-        copy_tile<D>(to, rq, qnxt, wave, 32 * (t + 1), RS);
-        copy_tile<D>(to, ro, onxt, wave, 32 * (t + 1), RS);
-        load_rows(32 * (t + 1), l2n, dln);
+      if (u + 1 < nu) {
+        int q0n, jn;
+        tile_of(u + 1, q0n, jn);
+        copy_tile<D>(to, rq, qnxt, wave, q0n, RSQ, (uint32_t)jn * D * 2);
+        copy_tile<D>(to, ro, onxt, wave, q0n, RSQ, (uint32_t)jn * D * 2);
+        load_rows(q0n, jn, l2n, dln);
       }
-      compute(qcur, ocur, 32 * t, l2c, dlc);
+      int q0t, j;
+      tile_of(u, q0t, j);
+      compute(qcur, ocur, q0t, l2c, dlc);
       wait_vmcnt<0>();
       barrier_all();
-  #pragma unroll
+#pragma unroll
       for (int g = 0; g < 4; ++g) {
         l2c[g] = l2n[g];
         dlc[g] = dln[g];
       }
     };
-    int t = t0;
-    for (; t + 1 < nqt; t += 2) {
-      step(t, Int<0>{});
-      step(t + 1, Int<1>{});
+    int u = 0;
+    for (; u + 1 < nu; u += 2) {
+      step(u, Int<0>{});
+      step(u + 1, Int<1>{});
     }
-    if (t < nqt) step(t, Int<0>{});
-
-
+    if (u < nu) step(u, Int<0>{});
   } else {
     // Software pipeline (one wave per SIMD, so no other wave fills the
-    // gaps): step t runs the S and dP products of tile t+1 interleaved with
-    // the VALU work of tile t (p and dS), then the dV and dK products of tile
-    // t. Q/dO tiles rotate through three LDS slots: step t reads tiles t
-    // (transposed) and t+1 (rows) while tile t+2 is copied in.
+    // gaps): step u runs the S and dP products of tile u+1 interleaved with
+    // the VALU work of tile u (p and dS), then the dV and dK products of tile
+    // u. Q/dO tiles rotate through three LDS slots: step u reads tiles u
+    // (transposed) and u+1 (rows) while tile u+2 is copied in.
+    f32x4 l2c[4], dlc[4], l2n[4], dln[4];
     f32x16 sc = f32x16{}, dpc = f32x16{};
     auto slot_q = [&](auto j) ATTN_INLINE -> char* {
       constexpr int J = decltype(j)::value % 3;
@@ -376,14 +402,19 @@ void dkdv_kernel(KernelArgs a) {
       constexpr int J = decltype(j)::value % 3;
       return J == 0 ? obuf0 : J == 1 ? obuf1 : obuf2;
     };
-    if (t0 < nqt) {
-      copy_tile<D>(to, rq, qbuf0, wave, 32 * t0, RS);
-      copy_tile<D>(to, ro, obuf0, wave, 32 * t0, RS);
-      if (t0 + 1 < nqt) {
-        copy_tile<D>(to, rq, qbuf1, wave, 32 * (t0 + 1), RS);
-        copy_tile<D>(to, ro, obuf1, wave, 32 * (t0 + 1), RS);
-      }
-      load_rows(32 * t0, l2c, dlc);
+    // copy tile u (Q and dO rows of its head) into slot st
+    auto copy_u = [&](int u, char* qd, char* od) ATTN_INLINE {
+      int q0t, j;
+      tile_of(u, q0t, j);
+      copy_tile<D>(to, rq, qd, wave, q0t, RSQ, (uint32_t)j * D * 2);
+      copy_tile<D>(to, ro, od, wave, q0t, RSQ, (uint32_t)j * D * 2);
+    };
+    if (nu > 0) {
+      copy_u(0, qbuf0, obuf0);
+      if (nu > 1) copy_u(1, qbuf1, obuf1);
+      int q0t, j;
+      tile_of(0, q0t, j);
+      load_rows(q0t, j, l2c, dlc);
       wait_vmcnt<0>();
       barrier_all();
 #pragma unroll
@@ -392,19 +423,21 @@ void dkdv_kernel(KernelArgs a) {
       for (int kc = 0; kc < KC; ++kc) dpc = E::mfma(row_op<D, T>(to, obuf0, kc), vreg[kc], dpc);
     }
     constexpr int NM = 2 * KC;  // S and dP MFMAs of one tile
-    auto pstep = [&](int t, auto j_tag, auto next_tag) ATTN_INLINE {
+    auto pstep = [&](int u, auto j_tag, auto next_tag) ATTN_INLINE {
       constexpr int J = decltype(j_tag)::value;
-      constexpr bool NEXT = decltype(next_tag)::value;  // tile t+1 exists
+      constexpr bool NEXT = decltype(next_tag)::value;  // tile u+1 exists
       const char* qn = slot_q(Int<J + 1>{});
       const char* on = slot_o(Int<J + 1>{});
-      if (t + 2 < nqt) {
-        copy_tile<D>(to, rq, slot_q(Int<J + 2>{}), wave, 32 * (t + 2), RS);
-        copy_tile<D>(to, ro, slot_o(Int<J + 2>{}), wave, 32 * (t + 2), RS);
+      if (u + 2 < nu) copy_u(u + 2, slot_q(Int<J + 2>{}), slot_o(Int<J + 2>{}));
+      if constexpr (NEXT) {
+        int q0n, jn;
+        tile_of(u + 1, q0n, jn);
+        load_rows(q0n, jn, l2n, dln);
       }
-      if (NEXT) load_rows(32 * (t + 1), l2n, dln);
       f32x16 sn = f32x16{}, dpn = f32x16{};
       float pv[16], dsv[16];
-      const int q0t = 32 * t;
+      int q0t, jcur;
+      tile_of(u, q0t, jcur);
       // operand ring: the LDS read of MFMA m + 2 is issued at step m
       v8 ring[2];
       auto opnd = [&](auto m_tag) ATTN_INLINE -> v8 {
@@ -428,7 +461,7 @@ void dkdv_kernel(KernelArgs a) {
         For<(m * 16) / NM, ((m + 1) * 16) / NM>::run([&](auto r_tag) ATTN_INLINE {
           constexpr int r = decltype(r_tag)::value;
           const int qr = q0t + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          const bool ok = qr < N && key < N && (!CAUSAL || key <= qr);
+          const bool ok = qr < Nq && key < Nk && (!CAUSAL || key <= qr + off);
           const float lse = l2c[r >> 2][r & 3];
           const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(sc[r], c, -lse * kLog2e)) : 0.f;
           pv[r] = p;
@@ -460,28 +493,28 @@ void dkdv_kernel(KernelArgs a) {
       }
     };
     // unrolled by three so every slot is a compile-time object
-    int t = t0;
-    for (; t + 3 < nqt; t += 3) {
-      pstep(t, Int<0>{}, TrueT{});
-      pstep(t + 1, Int<1>{}, TrueT{});
-      pstep(t + 2, Int<2>{}, TrueT{});
+    int u = 0;
+    for (; u + 3 < nu; u += 3) {
+      pstep(u, Int<0>{}, TrueT{});
+      pstep(u + 1, Int<1>{}, TrueT{});
+      pstep(u + 2, Int<2>{}, TrueT{});
     }
     // 0 to 3 tiles left (the last one without a next tile)
-    if (t + 2 < nqt) {
-      pstep(t, Int<0>{}, TrueT{});
-      pstep(t + 1, Int<1>{}, TrueT{});
-      pstep(t + 2, Int<2>{}, FalseT{});
-    } else if (t + 1 < nqt) {
-      pstep(t, Int<0>{}, TrueT{});
-      pstep(t + 1, Int<1>{}, FalseT{});
-    } else if (t < nqt) {
-      pstep(t, Int<0>{}, FalseT{});
+    if (u + 2 < nu) {
+      pstep(u, Int<0>{}, TrueT{});
+      pstep(u + 1, Int<1>{}, TrueT{});
+      pstep(u + 2, Int<2>{}, FalseT{});
+    } else if (u + 1 < nu) {
+      pstep(u, Int<0>{}, TrueT{});
+      pstep(u + 1, Int<1>{}, FalseT{});
+    } else if (u < nu) {
+      pstep(u, Int<0>{}, FalseT{});
     }
   }
 
-  if (key < N) {
-    if constexpr (DO_K) store_rows<D, T>((T*)a.dk + head_off, key, (uint32_t)a.H * D, h32, dkt, a.alpha);
-    if constexpr (DO_V) store_rows<D, T>((T*)a.dv + head_off, key, (uint32_t)a.H * D, h32, dvt, 1.0f);
+  if (key < Nk) {
+    if constexpr (DO_K) store_rows<D, T>((T*)a.dk + k_off, key, (uint32_t)a.Hkv * D, h32, dkt, a.alpha);
+    if constexpr (DO_V) store_rows<D, T>((T*)a.dv + k_off, key, (uint32_t)a.Hkv * D, h32, dvt, 1.0f);
   }
 #endif
 }
@@ -507,28 +540,32 @@ void dq_kernel(KernelArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h32 = lane >> 5, l32 = lane & 31;
 
-  const int BH = a.B * a.H;
+  const int BH = a.B * a.Hq;
   int mblk, bh;
-  decode_block(blockIdx.x, a.n_blk, BH, CAUSAL, mblk, bh);
-  const int b = bh / a.H, hh = bh % a.H;
-  const int N = a.N;
+  decode_block(blockIdx.x, a.n_qblk, BH, CAUSAL, mblk, bh);
+  const int b = bh / a.Hq, hq = bh % a.Hq;
+  const int hk = hq / a.g;                // the key/value head this head reads
+  const int Nq = a.Nq, Nk = a.Nk;
+  const int off = Nk - Nq;                // causal offset (bottom-right)
   const int q0 = mblk * 128;
   const int qi = q0 + 32 * wave + l32;    // this lane's query (column of S^T)
-  const uint32_t RS = (uint32_t)a.H * D * 2;
-  const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;
-  const uint32_t span = (uint32_t)(N - 1) * RS + D * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + head_off, span);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + head_off, span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + head_off, span);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.dout + head_off, span);
+  const uint32_t RSQ = (uint32_t)a.Hq * D * 2, RSK = (uint32_t)a.Hkv * D * 2;
+  const int64_t q_off = ((int64_t)b * Nq * a.Hq + hq) * D;
+  const int64_t k_off = ((int64_t)b * Nk * a.Hkv + hk) * D;
+  const uint32_t qspan = (uint32_t)(Nq - 1) * RSQ + D * 2;
+  const uint32_t kspan = Nk > 0 ? (uint32_t)(Nk - 1) * RSK + D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + q_off, qspan);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + k_off, kspan);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + k_off, kspan);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.dout + q_off, qspan);
 
   v8 qreg[KC], oreg[KC];
-  load_row_operand<D, T>(rq, (uint32_t)qi, RS, h32, qreg);
-  load_row_operand<D, T>(ro, (uint32_t)qi, RS, h32, oreg);
+  load_row_operand<D, T>(rq, (uint32_t)qi, RSQ, h32, qreg);
+  load_row_operand<D, T>(ro, (uint32_t)qi, RSQ, h32, oreg);
   TO to;
-  to.init(lane, wave, RS);
-  const float lse = qi < N ? a.lse[(int64_t)bh * N + qi] : 0.f;
-  const float dl = qi < N ? a.delta[(int64_t)bh * N + qi] : 0.f;
+  to.init(lane, wave, RSK);
+  const float lse = qi < Nq ? a.lse[(int64_t)bh * Nq + qi] : 0.f;
+  const float dl = qi < Nq ? a.delta[(int64_t)bh * Nq + qi] : 0.f;
   const bool live = lse != -__builtin_inff();
   const float l2 = live ? lse * kLog2e : 0.f;
 
@@ -537,8 +574,8 @@ void dq_kernel(KernelArgs a) {
   for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
   const float c = a.c;
 
-  const int kv_end = CAUSAL ? min(N, q0 + 128) : N;
-  const int nkt = (kv_end + 31) / 32;
+  const int kv_end = CAUSAL ? min(Nk, q0 + 128 + off) : Nk;
+  const int nkt = kv_end > 0 ? (kv_end + 31) / 32 : 0;
 
   auto compute = [&](const char* kt, const char* vt, int kv0) ATTN_INLINE {
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -550,7 +587,7 @@ void dq_kernel(KernelArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = kv0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      const bool ok = live && kr < N && (!CAUSAL || kr <= qi);
+      const bool ok = live && kr < Nk && (!CAUSAL || kr <= qi + off);
       const float p = ok ? exp2_fast(__builtin_fmaf(s[r], c, -l2)) : 0.f;
       dsv[r] = p * (dp[r] - dl);
     }
@@ -563,8 +600,8 @@ void dq_kernel(KernelArgs a) {
   };
 
   if (nkt > 0) {
-    copy_tile<D>(to, rk, kbuf0, wave, 0, RS);
-    copy_tile<D>(to, rv, vbuf0, wave, 0, RS);
+    copy_tile<D>(to, rk, kbuf0, wave, 0, RSK);
+    copy_tile<D>(to, rv, vbuf0, wave, 0, RSK);
     wait_vmcnt<0>();
     barrier_all();
   }
@@ -575,8 +612,8 @@ void dq_kernel(KernelArgs a) {
     char* knxt = J ? kbuf0 : kbuf1;
     char* vnxt = J ? vbuf0 : vbuf1;
     if (t + 1 < nkt) {
-      copy_tile<D>(to, rk, knxt, wave, 32 * (t + 1), RS);
-      copy_tile<D>(to, rv, vnxt, wave, 32 * (t + 1), RS);
+      copy_tile<D>(to, rk, knxt, wave, 32 * (t + 1), RSK);
+      copy_tile<D>(to, rv, vnxt, wave, 32 * (t + 1), RSK);
     }
     compute(kcur, vcur, 32 * t);
     wait_vmcnt<0>();
@@ -589,43 +626,50 @@ void dq_kernel(KernelArgs a) {
   }
   if (t < nkt) step(t, Int<0>{});
 
-  if (qi < N) store_rows<D, T>((T*)a.dq + head_off, qi, (uint32_t)a.H * D, h32, dqt, a.alpha);
+  if (qi < Nq) store_rows<D, T>((T*)a.dq + q_off, qi, (uint32_t)a.Hq * D, h32, dqt, a.alpha);
 #endif
 }
 
 template <int D, typename T>
 int launch_d(const BwdArgs& f, hipStream_t st) {
-  {
+  const int64_t qrows = (int64_t)f.B * f.N * f.H;
+  if (qrows > 0) {
     constexpr int RPB = 256 / (D / 8);
-    const int64_t rows = (int64_t)f.B * f.N * f.H;
-    const int grid = (int)((rows + RPB - 1) / RPB);
+    const int grid = (int)((qrows + RPB - 1) / RPB);
     hipLaunchKernelGGL((pre_kernel<D, T>), dim3(grid), dim3(256), 0, st, (const T*)f.o, (const T*)f.dout, f.delta,
                        f.B, f.H, f.N);
   }
   KernelArgs a;
   a.q = f.q; a.k = f.k; a.v = f.v; a.dout = f.dout; a.lse = f.lse; a.delta = f.delta;
   a.dq = f.dq; a.dk = f.dk; a.dv = f.dv;
-  a.B = f.B; a.H = f.H; a.N = f.N;
-  a.n_blk = (f.N + 127) / 128;
+  a.B = f.B; a.Hq = f.H; a.Hkv = f.Hkv; a.g = f.H / f.Hkv;
+  a.Nq = f.N; a.Nk = f.Nk;
+  a.n_kblk = (f.Nk + 127) / 128;
+  a.n_qblk = (f.N + 127) / 128;
   a.c = f.scale_log2;
   a.alpha = f.alpha;
-  const int grid = a.n_blk * f.B * f.H;
+  const int kgrid = a.n_kblk * f.B * f.Hkv;
+  const int qgrid = a.n_qblk * f.B * f.H;
   if (f.causal) {
-    if constexpr (D == 256) {
-      hipLaunchKernelGGL((dkdv_kernel<D, true, T, 1>), dim3(grid), dim3(256), 0, st, a);
-      hipLaunchKernelGGL((dkdv_kernel<D, true, T, 2>), dim3(grid), dim3(256), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, true, T, 3>), dim3(grid), dim3(256), 0, st, a);
+    if (kgrid > 0) {
+      if constexpr (D == 256) {
+        hipLaunchKernelGGL((dkdv_kernel<D, true, T, 1>), dim3(kgrid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((dkdv_kernel<D, true, T, 2>), dim3(kgrid), dim3(256), 0, st, a);
+      } else {
+        hipLaunchKernelGGL((dkdv_kernel<D, true, T, 3>), dim3(kgrid), dim3(256), 0, st, a);
+      }
     }
-    hipLaunchKernelGGL((dq_kernel<D, true, T>), dim3(grid), dim3(256), 0, st, a);
+    if (qgrid > 0) hipLaunchKernelGGL((dq_kernel<D, true, T>), dim3(qgrid), dim3(256), 0, st, a);
   } else {
-    if constexpr (D == 256) {
-      hipLaunchKernelGGL((dkdv_kernel<D, false, T, 1>), dim3(grid), dim3(256), 0, st, a);
-      hipLaunchKernelGGL((dkdv_kernel<D, false, T, 2>), dim3(grid), dim3(256), 0, st, a);
-    } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, false, T, 3>), dim3(grid), dim3(256), 0, st, a);
+    if (kgrid > 0) {
+      if constexpr (D == 256) {
+        hipLaunchKernelGGL((dkdv_kernel<D, false, T, 1>), dim3(kgrid), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((dkdv_kernel<D, false, T, 2>), dim3(kgrid), dim3(256), 0, st, a);
+      } else {
+        hipLaunchKernelGGL((dkdv_kernel<D, false, T, 3>), dim3(kgrid), dim3(256), 0, st, a);
+      }
     }
-    hipLaunchKernelGGL((dq_kernel<D, false, T>), dim3(grid), dim3(256), 0, st, a);
+    if (qgrid > 0) hipLaunchKernelGGL((dq_kernel<D, false, T>), dim3(qgrid), dim3(256), 0, st, a);
   }
   return (int)hipGetLastError();
 }

@@ -51,7 +51,8 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;
-  int B, H, N, d;
+  int B, H, N, d;    // H: query heads, N: query rows per batch entry
+  int Hkv, Nk;       // key/value heads (H % Hkv == 0), key rows
   int causal;
   int dtype;
   float alpha;       // alpha, clamped to >= 1e-30 / log2(e)

@@ -240,6 +240,24 @@ int attn_pack_gqa_heuristic(int Hq, int Hkv, int Nq);
  * 128 ranges. pack_gqa as in attn_fwd_ex. */
 int attn_num_splits_heuristic(int B, int Hq, int Hkv, int Nq, int Nk, int d, int pack_gqa, int num_cus);
 
+/*
+ * attn_bwd_ex -- attn_bwd for Hq query heads over Hkv key/value heads and
+ * N_q != N_k (dense [B, N, H, d] layouts).
+ *
+ *   q, o, dout, dq  [B, Nq, Hq, d];  k, v, dk, dv  [B, Nk, Hkv, d];
+ *   lse, delta      float32 [B, Hq, Nq] (lse from attn_fwd_ex, dense).
+ *   causal   bottom-right aligned, as in attn_fwd_ex.
+ *   The gradient of key/value head kh is the sum over the Hq / Hkv query
+ *   heads that read it ("FlashAttention-3 on Hopper", section 8.8): each
+ *   dK/dV workgroup loops over those heads' query tiles itself, so the sum
+ *   takes no atomics and the result is deterministic. Nq = 0 (or Nk = 0)
+ *   writes zero dK, dV (or dQ); the pointers of operands of size zero may
+ *   then be NULL. Other arguments and errors as attn_bwd.
+ */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                int causal, float alpha, int dtype, void* stream);
+
 /* Message of the last failed call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */
 const char* attn_last_error(void);

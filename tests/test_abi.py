@@ -151,6 +151,34 @@ def test_bwd_rejects_bad_arguments_before_launch(kw, status, msg):
     assert msg in ea.attn_last_error()
 
 
+def _bwd_ex(**kw):
+    lib = ea.load()
+    names = ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")
+    a = {n: FAKE + i * 0x10000000 for i, n in enumerate(names)}
+    a.update(dict(B=1, Hq=4, Hkv=2, Nq=100, Nk=300, d=128, causal=1, alpha=0.1, dtype=0, stream=None))
+    a.update(kw)
+    return lib.attn_bwd_ex(*(a[n] for n in names), a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                           a["causal"], a["alpha"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(Nk=-1), ea.ATTN_ERR_INVALID_ARG, ">= 0"),
+    (dict(dv=None), ea.ATTN_ERR_INVALID_ARG, "dv is null"),
+    (dict(dk=FAKE + 0x20000000), ea.ATTN_ERR_INVALID_ARG, "dk overlaps v"),
+    (dict(causal=5), ea.ATTN_ERR_INVALID_ARG, "causal"),
+])
+def test_bwd_ex_rejects_bad_arguments_before_launch(kw, status, msg):
+    assert _bwd_ex(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def test_bwd_ex_empty_problems_are_no_ops():
+    for kw in (dict(B=0), dict(Hq=0), dict(Nq=0, Nk=0)):
+        assert _bwd_ex(**kw) == ea.ATTN_OK, kw
+
+
 def test_bwd_empty_problem_is_a_no_op():
     assert _bwd(N=0) == ea.ATTN_OK
     assert _bwd(B=0) == ea.ATTN_OK

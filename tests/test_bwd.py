@@ -100,3 +100,49 @@ def test_bwd_head_dim_256_several_tiles(gpu, causal):
     # d = 256 runs the dK/dV kernel twice (dV, then dK)
     grads, vals, do_vals, _ = _run(gpu, 1, 700, 2, 256, causal, seed=13)
     _check(grads, vals, do_vals, causal, tag=("d256", causal))
+
+
+def _run_gqa(ea, B, Nq, Nk, Hq, Hkv, d, causal, seed=0):
+    import torch
+    from synth_inputs import make_qkv_gqa
+    bits, vals = make_qkv_gqa(B, Nq, Nk, Hq, Hkv, d, seed=seed)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda() for b in bits)
+    dbits, dvals = make_dout(B, Nq, Hq, d, seed=seed)
+    do = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+    o, lse = ea.attention_ex(q, k, v, causal=causal, pack_gqa=0, num_splits=1)
+    grads = ea.attention_backward_ex(q, k, v, o, lse, do, causal=causal)
+    torch.cuda.synchronize()
+    return grads, vals, dvals
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (6, 1), (3, 3)])
+def test_bwd_grouped_heads(gpu, d, hq, hkv):
+    from oracle.attention_bwd import attention_backward_gqa
+    for nq, nk, causal in ((150, 150, False), (77, 300, True), (300, 77, True), (200, 130, False)):
+        grads, vals, dvals = _run_gqa(gpu, 2, nq, nk, hq, hkv, d, causal, seed=d + hq + nq)
+        refs = attention_backward_gqa(*vals, dvals, None, causal)
+        for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
+            e = _rel(to_f64(g), r)
+            assert np.isfinite(to_f64(g)).all(), (d, hq, hkv, nq, nk, name)
+            assert e["rel_max"] <= REL_MAX and e["rel_rms"] <= REL_RMS, (d, hq, hkv, nq, nk, causal, name, e)
+
+
+def test_bwd_grouped_heads_deterministic_and_empty_queries(gpu):
+    import torch
+    grads1, _, _ = _run_gqa(gpu, 1, 257, 513, 8, 2, 128, True, seed=3)
+    grads2, _, _ = _run_gqa(gpu, 1, 257, 513, 8, 2, 128, True, seed=3)
+    for a, b in zip(grads1, grads2):
+        assert torch.equal(a, b)
+    # keys that no query sees (causal, N_q < N_k: keys past the last query's
+    # diagonal do not exist; the first N_k - N_q keys are seen by every row)
+    # and N_q = 0: dK = dV = 0
+    k = torch.randn((1, 64, 2, 64), device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, 64, 2, 64), device="cuda").to(torch.bfloat16)
+    q = torch.empty((1, 0, 4, 64), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((1, 4, 0), device="cuda", dtype=torch.float32)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    gpu.attn_bwd_ex(q, k, v, q, q, lse, torch.empty_like(q), dk, dv, torch.empty_like(lse), causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
