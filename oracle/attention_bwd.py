@@ -24,12 +24,13 @@ import numpy as np
 
 from .attention import causal_mask
 
-__all__ = ["attention_backward", "attention_backward_head", "attention_backward_gqa"]
+__all__ = ["attention_backward", "attention_backward_head", "attention_backward_gqa", "attention_backward_varlen"]
 
 
-def attention_backward_head(q, k, v, do, alpha, causal=False, row_chunk=1024):
+def attention_backward_head(q, k, v, do, alpha, causal=False, row_chunk=1024, mask=None):
     """Gradients (dq, dk, dv) of one head: q, do are (N_q, d), k, v are
-    (N_k, d) float64; causal uses the bottom-right alignment of the forward."""
+    (N_k, d) float64; causal uses the bottom-right alignment of the forward,
+    and ``mask`` is a further (N_q, N_k) boolean array of excluded entries."""
     n = q.shape[0]
     nk = k.shape[0]
     dq = np.zeros_like(q)
@@ -40,6 +41,8 @@ def attention_backward_head(q, k, v, do, alpha, causal=False, row_chunk=1024):
         s = alpha * (q[r0:r1] @ k.T)
         if causal:
             s = np.where(causal_mask(n, nk)[r0:r1], -np.inf, s)
+        if mask is not None:
+            s = np.where(np.asarray(mask, dtype=bool)[r0:r1], -np.inf, s)
         m = s.max(axis=1, keepdims=True)
         live = np.isfinite(m)
         e = np.where(live, np.exp(s - np.where(live, m, 0.0)), 0.0)
@@ -77,7 +80,7 @@ def attention_backward(q, k, v, do, alpha=None, causal=False, row_chunk=1024):
     return dq, dk, dv
 
 
-def attention_backward_gqa(q, k, v, do, alpha=None, causal=False):
+def attention_backward_gqa(q, k, v, do, alpha=None, causal=False, window=(-1, -1)):
     """Gradients for H_q query heads over H_kv key/value heads.
 
     q, do are (B, N_q, H_q, d); k, v are (B, N_k, H_kv, d). Query head h
@@ -100,11 +103,40 @@ def attention_backward_gqa(q, k, v, do, alpha=None, causal=False):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    from .variants import window_mask
+    mask = window_mask(nq, k.shape[1], *window)
     for b in range(B):
         for h in range(hq):
             kh = h // g
-            gq, gk, gv = attention_backward_head(q[b, :, h], k[b, :, kh], v[b, :, kh], do[b, :, h], alpha, causal)
+            gq, gk, gv = attention_backward_head(q[b, :, h], k[b, :, kh], v[b, :, kh], do[b, :, h], alpha, causal,
+                                                 mask=mask)
             dq[b, :, h] = gq
             dk[b, :, kh] += gk
             dv[b, :, kh] += gv
+    return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, do, cu_q, cu_k, alpha=None, causal=False, window=(-1, -1)):
+    """Gradients of a packed variable-length batch: q, do (total_q, H_q, d),
+    k, v (total_k, H_kv, d); sequence b owns rows cu[b] .. cu[b+1]-1 and is an
+    independent problem (the forward's reading of packed batches)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    if alpha is None:
+        alpha = 1.0 / np.sqrt(q.shape[2])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(cu_q.size - 1):
+        sq = slice(cu_q[b], cu_q[b + 1])
+        sk = slice(cu_k[b], cu_k[b + 1])
+        if cu_q[b + 1] == cu_q[b] or cu_k[b + 1] == cu_k[b]:
+            continue
+        gq, gk, gv = attention_backward_gqa(q[None, sq], k[None, sk], v[None, sk], do[None, sq], alpha, causal,
+                                            window)
+        dq[sq], dk[sk], dv[sk] = gq[0], gk[0], gv[0]
     return dq, dk, dv

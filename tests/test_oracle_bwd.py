@@ -146,3 +146,50 @@ def test_gqa_backward_with_one_group_is_mha():
         b = attention_backward(q, k, v, do, 0.5, causal)
         for x, y in zip(a, b):
             np.testing.assert_allclose(x, y, rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("window", [(1, 0), (2, 1), (-1, 1), (0, -1)])
+def test_windowed_backward_matches_central_differences(window):
+    from oracle.attention_bwd import attention_backward_gqa
+    from oracle.variants import attention_gqa
+    B, nq, nk, hq, hkv, d = 1, 5, 7, 2, 1, 3
+    q, do = _rand((B, nq, hq, d), 70), _rand((B, nq, hq, d), 71)
+    k, v = _rand((B, nk, hkv, d), 72), _rand((B, nk, hkv, d), 73)
+    dq, dk, dv = attention_backward_gqa(q, k, v, do, 0.8, False, window)
+
+    def loss(q_, k_, v_):
+        o, _ = attention_gqa(q_, k_, v_, 0.8, False, window=window)
+        return float(np.sum(o * do))
+    eps = 1e-6
+    for name, x, gr in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"])
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(gr, fd, rtol=1e-6, atol=1e-8, err_msg=f"{name} {window}")
+
+
+def test_varlen_backward_is_per_sequence():
+    from oracle.attention_bwd import attention_backward_gqa, attention_backward_varlen
+    lq, lk = [3, 0, 5, 2], [4, 3, 5, 0]
+    cu_q = np.concatenate([[0], np.cumsum(lq)])
+    cu_k = np.concatenate([[0], np.cumsum(lk)])
+    hq, hkv, d = 4, 2, 3
+    q, do = _rand((cu_q[-1], hq, d), 80), _rand((cu_q[-1], hq, d), 81)
+    k, v = _rand((cu_k[-1], hkv, d), 82), _rand((cu_k[-1], hkv, d), 83)
+    dq, dk, dv = attention_backward_varlen(q, k, v, do, cu_q, cu_k, 0.7, True, (2, 0))
+    for b in range(4):
+        sq, sk = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        if lq[b] and lk[b]:
+            g = attention_backward_gqa(q[None, sq], k[None, sk], v[None, sk], do[None, sq], 0.7, True, (2, 0))
+            np.testing.assert_allclose(dq[sq], g[0][0], rtol=1e-14)
+            np.testing.assert_allclose(dk[sk], g[1][0], rtol=1e-14)
+        else:
+            # a sequence without keys (or queries) has no gradient
+            assert np.all(dq[sq] == 0) and np.all(dk[sk] == 0) and np.all(dv[sk] == 0)
