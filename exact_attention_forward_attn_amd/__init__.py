@@ -31,8 +31,9 @@ max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, workspace=None,
 ``attn_splitkv_workspace_bytes``, ``attn_pack_gqa_heuristic``,
 ``attn_num_splits_heuristic``
     Sizing helpers of attn_fwd_ex (pure host functions).
-``attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None)``
-    Backward with Hq query heads over Hkv key/value heads and N_q != N_k.
+``attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None,
+  cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, window=(-1, -1))``
+    Backward with grouped heads, N_q != N_k, packed batches and windows.
 ``attn_last_error()``
     Message of the last failed call on this thread.
 
@@ -95,7 +96,8 @@ def load():
     lib.attn_fwd_fp8.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_bwd.restype = i
-    lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, i, i,
+                                f, i, vp]
     lib.attn_bwd_ex.restype = i
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, i, i, f, i, i, i, vp,
                                 ctypes.c_int64, vp]
@@ -316,38 +318,46 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None,
     return dq, dk, dv
 
 
-def attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None):
-    """Backward with Hq query heads over Hkv key/value heads and N_q != N_k:
-    q, o, dout, dq [B, Nq, Hq, d]; k, v, dk, dv [B, Nk, Hkv, d]; lse and
-    delta float32 [B, Hq, Nq]."""
+def attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None,
+                cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, window=(-1, -1)):
+    """Backward with Hq query heads over Hkv key/value heads, N_q != N_k,
+    packed batches and a (left, right) sliding window. Dense: q, o, dout, dq
+    [B, Nq, Hq, d]; k, v, dk, dv [B, Nk, Hkv, d]; lse and delta float32
+    [B, Hq, Nq]. Packed: [total_q, Hq, d], [total_k, Hkv, d], [Hq, total_q]."""
     torch = _torch()
     lib = load()
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q must be [B, Nq, Hq, d] and k [B, Nk, Hkv, d]")
-    B, Nq, Hq, d = q.shape
-    Nk, Hkv = k.shape[1], k.shape[2]
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError("q must be bfloat16 or float16")
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    B, Hq, Hkv, Nq, Nk, d, total_q, total_k, lse_shape = _ex_shapes(q, k, cu_seqlens_q, cu_seqlens_k,
+                                                                    max_seqlen_q, max_seqlen_k)
     for t, n in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
         _require(t, n, q.dtype, q.shape, q.device)
     for t, n in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
         _require(t, n, q.dtype, k.shape, q.device)
-    _require(lse, "lse", torch.float32, (B, Hq, Nq), q.device)
-    _require(delta, "delta", torch.float32, (B, Hq, Nq), q.device)
+    _require(lse, "lse", torch.float32, lse_shape, q.device)
+    _require(delta, "delta", torch.float32, lse_shape, q.device)
+    cu_q = cu_k = ctypes.c_void_p(0)
+    if cu_seqlens_q is not None:
+        _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,), q.device)
+        _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, (B + 1,), q.device)
+        cu_q, cu_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
     dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
     _check(lib.attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                           _ptr(delta), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), _default_alpha(d, alpha), dt,
-                           _stream_handle(stream)))
+                           _ptr(delta), B, Hq, Hkv, Nq, Nk, d, cu_q, cu_k, total_q, total_k, int(bool(causal)),
+                           int(window[0]), int(window[1]), _default_alpha(d, alpha), dt, _stream_handle(stream)))
     return dq, dk, dv
 
 
-def attention_backward_ex(q, k, v, o, lse, dout, causal=False, alpha=None, stream=None):
+def attention_backward_ex(q, k, v, o, lse, dout, causal=False, alpha=None, stream=None, cu_seqlens_q=None,
+                          cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, window=(-1, -1)):
     """Allocate dq, dk, dv and the workspace with torch and run attn_bwd_ex."""
     torch = _torch()
-    B, Nq, Hq, d = q.shape
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    return attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal, alpha, stream)
+    delta = torch.empty(lse.shape, dtype=torch.float32, device=q.device)
+    return attn_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, delta, causal, alpha, stream, cu_seqlens_q, cu_seqlens_k,
+                       max_seqlen_q, max_seqlen_k, window)
 
 
 def attention_backward(q, k, v, o, lse, dout, causal=False, alpha=None, stream=None):

@@ -298,6 +298,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
   a.B = B; a.H = H; a.N = N; a.d = d;
   a.Hkv = H; a.Nk = N;
+  a.win_l = 2 * N + 1;  // unbounded left
+  a.win_r = 0;          // causal (used only when causal = 1)
   a.causal = causal;
   a.dtype = dtype;
   a.scale_log2 = scale_log2(alpha);
@@ -307,7 +309,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                 void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                int causal, float alpha, int dtype, void* stream) {
+                const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q, int total_k, int causal,
+                int window_left, int window_right, float alpha, int dtype, void* stream) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
@@ -318,19 +321,34 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
   if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0))
     return fail(ATTN_ERR_INVALID_ARG, "Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (window_left < -1 || window_right < -1)
+    return fail(ATTN_ERR_INVALID_ARG, "window widths must be >= -1 (got %d, %d)", window_left, window_right);
   if (!std::isfinite(alpha) || alpha < 0.f)
     return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
-  if (B == 0 || Hq == 0 || (Nq == 0 && Nk == 0)) return ok();
+  const bool varlen = cu_seqlens_q != nullptr || cu_seqlens_k != nullptr;
+  if (varlen && (!cu_seqlens_q || !cu_seqlens_k))
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must both be given or both be null");
+  if (varlen && (total_q < 0 || total_k < 0))
+    return fail(ATTN_ERR_INVALID_ARG, "total_q, total_k must be >= 0 (got %d, %d)", total_q, total_k);
+  if (!varlen) {
+    if ((int64_t)B * Nq >= (int64_t(1) << 31) || (int64_t)B * Nk >= (int64_t(1) << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, "B*Nq or B*Nk too large (>= 2^31)");
+    total_q = B * Nq;
+    total_k = B * Nk;
+  }
+  if (B == 0 || Hq == 0 || (total_q == 0 && total_k == 0)) return ok();
   if (((int64_t)Nq + 128) * Hq * d * 2 >= (int64_t(1) << 31) || ((int64_t)Nk + 128) * Hkv * d * 2 >= (int64_t(1) << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "sequence too long for the number of heads (N*H*d*2 near 2^31)");
-  if ((int64_t)B * Hq * Nq >= (int64_t(1) << 31) || (int64_t)B * Hkv * Nk >= (int64_t(1) << 31))
-    return fail(ATTN_ERR_UNSUPPORTED, "B*H*N too large (>= 2^31)");
+  if ((int64_t)total_q * Hq >= (int64_t(1) << 31) || (int64_t)total_k * Hkv >= (int64_t(1) << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "total rows * heads too large (>= 2^31)");
+  if (varlen && ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u)))
+    return fail(ATTN_ERR_INVALID_ARG, "cu_seqlens are not 4-byte aligned");
   const void* ptrs[10] = {q, k, v, o, dout, lse, dq, dk, dv, delta};
   const char* names[10] = {"q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta"};
-  const int64_t qb = (int64_t)B * Nq * Hq * d * 2, kb = (int64_t)B * Nk * Hkv * d * 2;
-  const int64_t rb = (int64_t)B * Hq * Nq * 4;
+  const int64_t qb = (int64_t)total_q * Hq * d * 2, kb = (int64_t)total_k * Hkv * d * 2;
+  const int64_t rb = (int64_t)total_q * Hq * 4;
   const int64_t bytes[10] = {qb, kb, kb, qb, qb, rb, qb, kb, kb, rb};
-  // operands of size zero (Nq = 0 or Nk = 0) may be null
+  // operands of size zero (no query or no key rows) may be null
   for (int i = 0; i < 10; ++i) {
     if (bytes[i] == 0) continue;
     if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
@@ -345,7 +363,15 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
   a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
   a.B = B; a.H = Hq; a.N = Nq; a.d = d;
   a.Hkv = Hkv; a.Nk = Nk;
-  a.causal = causal;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.total_q = total_q; a.total_k = total_k;
+  // same window convention as attn_fwd_ex: causal is a right width of 0 and
+  // an unbounded side is any width past the sequence
+  const int wide = Nq + Nk + 1;
+  a.win_l = window_left < 0 ? wide : (window_left < wide ? window_left : wide);
+  a.win_r = window_right < 0 ? wide : (window_right < wide ? window_right : wide);
+  if (causal) a.win_r = 0;
+  a.causal = (causal || window_left >= 0 || window_right >= 0) ? 1 : 0;
   a.dtype = dtype;
   a.scale_log2 = scale_log2(alpha);
   a.alpha = a.scale_log2 / 1.4426950408889634f;

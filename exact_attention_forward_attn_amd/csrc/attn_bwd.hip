@@ -42,15 +42,18 @@ using namespace attn::dev;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- D = rowsum(dO o O) ------------------------------------------------------
-// rows in memory order r = (b*N + n)*H + h; D_i is stored as delta[(b*H + h)*N + n]
+// rows in memory order r = row*H + h with row = b*N + n (dense) or the packed
+// row (varlen); D_i is stored like LSE: delta[(b*H + h)*N + n], or
+// delta[h*total + row] for packed batches (total > 0)
 template <int D, typename T>
-__global__ __launch_bounds__(256) void pre_kernel(const T* o, const T* dout, float* delta, int B, int H, int N) {
+__global__ __launch_bounds__(256) void pre_kernel(const T* o, const T* dout, float* delta, int B, int H, int N,
+                                                  int total) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int LPR = D / 8;       // lanes per row, 8 elements each
   constexpr int RPB = 256 / LPR;   // rows per workgroup
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int li = threadIdx.x % LPR;
-  const int64_t nrows = (int64_t)B * N * H;
+  const int64_t nrows = total > 0 ? (int64_t)total * H : (int64_t)B * N * H;
   float acc = 0.f;
   if (row < nrows) {
     typedef T t8 __attribute__((ext_vector_type(8)));
@@ -63,8 +66,12 @@ __global__ __launch_bounds__(256) void pre_kernel(const T* o, const T* dout, flo
   for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < nrows && li == 0) {
     const int64_t h = row % H, bn = row / H;
-    const int64_t n = bn % N, b = bn / N;
-    delta[(b * H + h) * N + n] = acc;
+    if (total > 0) {
+      delta[h * total + bn] = acc;
+    } else {
+      const int64_t n = bn % N, b = bn / N;
+      delta[(b * H + h) * N + n] = acc;
+    }
   }
 #endif
 }
@@ -83,9 +90,29 @@ struct KernelArgs {
   int Nq, Nk;         // query and key rows per batch entry
   int n_kblk;         // ceil(Nk / 128): dK/dV workgroups per (b, KV head)
   int n_qblk;         // ceil(Nq / 128): dQ workgroups per (b, query head)
+  const int* cu_q;    // packed batches: row offsets (Nq, Nk are then maxima)
+  const int* cu_k;
+  int total_q, total_k;
+  int win_l, win_r;   // masked kernels: query n sees key j iff
+                      // n + off - win_l <= j <= n + off + win_r
   float c;            // alpha * log2(e)
   float alpha;
 };
+
+// Rows of batch entry b in q/o and k/v: dense strides or clamped packed
+// offsets (malformed offsets never address outside the tensors).
+__device__ __forceinline__ void seq_extent(const KernelArgs& a, int b, int& q_row0, int& len_q, int& k_row0,
+                                           int& len_k) {
+  if (a.cu_q) {
+    q_row0 = min(max(a.cu_q[b], 0), a.total_q);
+    len_q = min(min(max(a.cu_q[b + 1], q_row0), a.total_q) - q_row0, a.Nq);
+    k_row0 = min(max(a.cu_k[b], 0), a.total_k);
+    len_k = min(min(max(a.cu_k[b + 1], k_row0), a.total_k) - k_row0, a.Nk);
+  } else {
+    q_row0 = b * a.Nq; len_q = a.Nq;
+    k_row0 = b * a.Nk; len_k = a.Nk;
+  }
+}
 
 // waves per SIMD each kernel is compiled for (its register budget): dK/dV
 // keeps K, V, dK^T and dV^T in registers
@@ -253,23 +280,29 @@ void dkdv_kernel(KernelArgs a) {
   decode_block(blockIdx.x, a.n_kblk, BH, CAUSAL, kblk, bh);
   if (CAUSAL) kblk = a.n_kblk - 1 - kblk;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
-  const int Nq = a.Nq, Nk = a.Nk, grp = a.g;
-  const int off = Nk - Nq;                // causal offset (bottom-right)
+  const int grp = a.g;
+  int q_row0, Nq, k_row0, Nk;             // this batch entry's rows and lengths
+  seq_extent(a, b, q_row0, Nq, k_row0, Nk);
   const int k0 = kblk * 128;
+  if (k0 >= Nk) return;                   // past a short key sequence (uniform)
+  const int off = Nk - Nq;                // causal offset (bottom-right)
   const int key = k0 + 32 * wave + l32;   // this lane's key (column of S)
   const uint32_t RSQ = (uint32_t)a.Hq * D * 2, RSK = (uint32_t)a.Hkv * D * 2;
-  const int64_t k_off = ((int64_t)b * Nk * a.Hkv + hk) * D;
-  const int64_t q_off = ((int64_t)b * Nq * a.Hq + (int64_t)hk * grp) * D;  // first head of the group
+  const int64_t k_off = ((int64_t)k_row0 * a.Hkv + hk) * D;
+  const int64_t q_off = ((int64_t)q_row0 * a.Hq + (int64_t)hk * grp) * D;  // first head of the group
   const uint32_t kspan = (uint32_t)(Nk - 1) * RSK + D * 2;
   const uint32_t qspan = Nq > 0 ? (uint32_t)(Nq - 1) * RSQ + (uint32_t)grp * D * 2 : 0;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + q_off, qspan);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + k_off, kspan);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + k_off, kspan);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.dout + q_off, qspan);
-  // LSE and D of the group's heads: [g][Nq] from (b, first head)
-  const int64_t l_off = ((int64_t)b * a.Hq + (int64_t)hk * grp) * Nq;
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + l_off, (uint32_t)grp * Nq * 4);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + l_off, (uint32_t)grp * Nq * 4);
+  // LSE and D of the group's heads, head j at l_off + j * l_hs: [B, Hq, Nq]
+  // for dense inputs, [Hq, total_q] for packed batches
+  const int64_t l_off = a.cu_q ? (int64_t)hk * grp * a.total_q + q_row0 : ((int64_t)b * a.Hq + (int64_t)hk * grp) * a.Nq;
+  const uint32_t l_hs = a.cu_q ? (uint32_t)a.total_q : (uint32_t)a.Nq;
+  const uint32_t lspan = Nq > 0 ? ((uint32_t)(grp - 1) * l_hs + (uint32_t)Nq) * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + l_off, lspan);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + l_off, lspan);
 
   v8 kreg[KC], vreg[DO_K ? KC : 1];
   load_row_operand<D, T>(rk, (uint32_t)key, RSK, h32, kreg);
@@ -294,22 +327,40 @@ void dkdv_kernel(KernelArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = q0t + 8 * g + 4 * h32 + e;
-        const uint32_t lo = row < Nq ? ((uint32_t)j * Nq + row) * 4 : 0xffffffffu;
+        const uint32_t lo = row < Nq ? ((uint32_t)j * l_hs + row) * 4 : 0xffffffffu;
         l2[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0));
         dl[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lo, 0, 0));
       }
   };
 
-  // query tiles of one head: query n sees key k iff k <= n + off, so rows
-  // below k0 - off meet none of these keys; the loop runs over
-  // (head of the group, tile) pairs u = j * nt_h + (t - t0)
+  // query tiles of one head: in the masked instantiation query n sees key k
+  // iff n + off - win_l <= k <= n + off + win_r, so only the tiles of rows
+  // k0 - off - win_r .. k0 + 127 - off + win_l meet these keys; the loop runs
+  // over (head of the group, tile) pairs u = j * nt_h + (t - t0)
   const int nqt = (Nq + 31) / 32;
-  const int t0 = CAUSAL ? min(nqt, max(0, k0 - off) / 32) : 0;
-  const int nt_h = nqt - t0;
+  int t0 = 0, t1 = nqt;
+  if (CAUSAL) {
+    t0 = min(nqt, max(0, k0 - off - a.win_r) / 32);
+    const int hi = k0 + 127 - off + a.win_l;
+    t1 = hi < 0 ? 0 : min(nqt, hi / 32 + 1);
+  }
+  const int nt_h = max(0, t1 - t0);
   const int nu = grp * nt_h;
   auto tile_of = [&](int u, int& q0t, int& j) ATTN_INLINE {
     j = u / nt_h;
     q0t = 32 * (t0 + u - j * nt_h);
+  };
+
+  // Band test of score r of a lane (row q0t + 4*h32 + 8*(r>>2) + (r&3), the
+  // lane's key): the row sees the key iff 0 <= key - row - off + win_l <=
+  // win_l + win_r, one unsigned compare against a per-tile base. Rows past
+  // Nq need no test: their Q and dO rows read as zero (and LSE, D as 0), so
+  // p = 1 and dS = 0 add nothing; keys past Nk only reach their own dK/dV
+  // rows, which are not stored.
+  const uint32_t wspan = (uint32_t)(a.win_l + a.win_r);
+  auto band_base = [&](int q0t) ATTN_INLINE { return key - q0t - 4 * h32 - off + a.win_l; };
+  auto in_band = [&](int kb, int r) ATTN_INLINE {
+    return (uint32_t)(kb - (8 * (r >> 2) + (r & 3))) <= wspan;
   };
 
   auto compute = [&](const char* qt, const char* ot, int q0t, const f32x4 (&l2)[4], const f32x4 (&dl)[4]) ATTN_INLINE {
@@ -321,10 +372,10 @@ void dkdv_kernel(KernelArgs a) {
       for (int kc = 0; kc < KC; ++kc) dp = E::mfma(row_op<D, T>(to, ot, kc), vreg[kc], dp);
     }
     float pv[16], dsv[16];
+    const int kb = band_base(q0t);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int qr = q0t + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      const bool ok = qr < Nq && key < Nk && (!CAUSAL || key <= qr + off);
+      const bool ok = !CAUSAL || in_band(kb, r);
       const float lse = l2[r >> 2][r & 3];
       // a row with LSE = -inf has no keys; its p stays 0
       const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(s[r], c, -lse * kLog2e)) : 0.f;
@@ -438,6 +489,7 @@ void dkdv_kernel(KernelArgs a) {
       float pv[16], dsv[16];
       int q0t, jcur;
       tile_of(u, q0t, jcur);
+      const int kb = band_base(q0t);
       // operand ring: the LDS read of MFMA m + 2 is issued at step m
       v8 ring[2];
       auto opnd = [&](auto m_tag) ATTN_INLINE -> v8 {
@@ -460,8 +512,7 @@ void dkdv_kernel(KernelArgs a) {
         // p and dS of the scores assigned to this step
         For<(m * 16) / NM, ((m + 1) * 16) / NM>::run([&](auto r_tag) ATTN_INLINE {
           constexpr int r = decltype(r_tag)::value;
-          const int qr = q0t + 8 * (r >> 2) + 4 * h32 + (r & 3);
-          const bool ok = qr < Nq && key < Nk && (!CAUSAL || key <= qr + off);
+          const bool ok = !CAUSAL || in_band(kb, r);
           const float lse = l2c[r >> 2][r & 3];
           const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(sc[r], c, -lse * kLog2e)) : 0.f;
           pv[r] = p;
@@ -545,13 +596,15 @@ void dq_kernel(KernelArgs a) {
   decode_block(blockIdx.x, a.n_qblk, BH, CAUSAL, mblk, bh);
   const int b = bh / a.Hq, hq = bh % a.Hq;
   const int hk = hq / a.g;                // the key/value head this head reads
-  const int Nq = a.Nq, Nk = a.Nk;
-  const int off = Nk - Nq;                // causal offset (bottom-right)
+  int q_row0, Nq, k_row0, Nk;             // this batch entry's rows and lengths
+  seq_extent(a, b, q_row0, Nq, k_row0, Nk);
   const int q0 = mblk * 128;
+  if (q0 >= Nq) return;                   // past a short query sequence (uniform)
+  const int off = Nk - Nq;                // causal offset (bottom-right)
   const int qi = q0 + 32 * wave + l32;    // this lane's query (column of S^T)
   const uint32_t RSQ = (uint32_t)a.Hq * D * 2, RSK = (uint32_t)a.Hkv * D * 2;
-  const int64_t q_off = ((int64_t)b * Nq * a.Hq + hq) * D;
-  const int64_t k_off = ((int64_t)b * Nk * a.Hkv + hk) * D;
+  const int64_t q_off = ((int64_t)q_row0 * a.Hq + hq) * D;
+  const int64_t k_off = ((int64_t)k_row0 * a.Hkv + hk) * D;
   const uint32_t qspan = (uint32_t)(Nq - 1) * RSQ + D * 2;
   const uint32_t kspan = Nk > 0 ? (uint32_t)(Nk - 1) * RSK + D * 2 : 0;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + q_off, qspan);
@@ -564,8 +617,9 @@ void dq_kernel(KernelArgs a) {
   load_row_operand<D, T>(ro, (uint32_t)qi, RSQ, h32, oreg);
   TO to;
   to.init(lane, wave, RSK);
-  const float lse = qi < Nq ? a.lse[(int64_t)bh * Nq + qi] : 0.f;
-  const float dl = qi < Nq ? a.delta[(int64_t)bh * Nq + qi] : 0.f;
+  const int64_t li = a.cu_q ? (int64_t)hq * a.total_q + q_row0 + qi : (int64_t)bh * a.Nq + qi;
+  const float lse = qi < Nq ? a.lse[li] : -__builtin_inff();
+  const float dl = qi < Nq ? a.delta[li] : 0.f;
   const bool live = lse != -__builtin_inff();
   const float l2 = live ? lse * kLog2e : 0.f;
 
@@ -574,10 +628,27 @@ void dq_kernel(KernelArgs a) {
   for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
   const float c = a.c;
 
-  const int kv_end = CAUSAL ? min(Nk, q0 + 128 + off) : Nk;
-  const int nkt = kv_end > 0 ? (kv_end + 31) / 32 : 0;
+  // keys some row of the block sees (masked: from q0 + off - win_l to
+  // q0 + 127 + off + win_r), in tiles starting at tile tk0
+  int kv_lo = 0, kv_end = Nk;
+  if (CAUSAL) {
+    kv_lo = min(Nk, max(0, q0 + off - a.win_l));
+    kv_end = min(Nk, q0 + 128 + off + a.win_r);
+  }
+  const int tk0 = kv_lo / 32;
+  const int nkt = kv_end > 32 * tk0 ? (kv_end - 32 * tk0 + 31) / 32 : 0;
 
   auto compute = [&](const char* kt, const char* vt, int kv0) ATTN_INLINE {
+    // keys this lane's row sees, relative to the lane's first key of the tile
+    // (kv0 + 4*h32); a row past Nq or with LSE = -inf sees none
+    const int base = kv0 + 4 * h32;
+    int lo = CAUSAL ? qi + off - a.win_l - base : -base;
+    const int hi = min(Nk - 1, CAUSAL ? qi + off + a.win_r : Nk) - base;
+    uint32_t span = (uint32_t)(hi - lo);
+    if (!live || hi < lo) {
+      lo = 1 << 30;
+      span = 0;
+    }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) s = E::mfma(row_op<D, T>(to, kt, kc), qreg[kc], s);
@@ -586,8 +657,11 @@ void dq_kernel(KernelArgs a) {
     float dsv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kr = kv0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-      const bool ok = live && kr < Nk && (!CAUSAL || kr <= qi + off);
+      // key kv0 + 4*h32 + cr, cr = 8*(r>>2) + (r&3), is seen iff cr - lo
+      // lies in [0, span] (unsigned); the span also stops at Nk, since a
+      // zero-filled key row past Nk could make p overflow
+      const int cr = 8 * (r >> 2) + (r & 3);
+      const bool ok = (uint32_t)(cr - lo) <= span;
       const float p = ok ? exp2_fast(__builtin_fmaf(s[r], c, -l2)) : 0.f;
       dsv[r] = p * (dp[r] - dl);
     }
@@ -600,8 +674,8 @@ void dq_kernel(KernelArgs a) {
   };
 
   if (nkt > 0) {
-    copy_tile<D>(to, rk, kbuf0, wave, 0, RSK);
-    copy_tile<D>(to, rv, vbuf0, wave, 0, RSK);
+    copy_tile<D>(to, rk, kbuf0, wave, 32 * tk0, RSK);
+    copy_tile<D>(to, rv, vbuf0, wave, 32 * tk0, RSK);
     wait_vmcnt<0>();
     barrier_all();
   }
@@ -612,10 +686,10 @@ void dq_kernel(KernelArgs a) {
     char* knxt = J ? kbuf0 : kbuf1;
     char* vnxt = J ? vbuf0 : vbuf1;
     if (t + 1 < nkt) {
-      copy_tile<D>(to, rk, knxt, wave, 32 * (t + 1), RSK);
-      copy_tile<D>(to, rv, vnxt, wave, 32 * (t + 1), RSK);
+      copy_tile<D>(to, rk, knxt, wave, 32 * (tk0 + t + 1), RSK);
+      copy_tile<D>(to, rv, vnxt, wave, 32 * (tk0 + t + 1), RSK);
     }
-    compute(kcur, vcur, 32 * t);
+    compute(kcur, vcur, 32 * (tk0 + t));
     wait_vmcnt<0>();
     barrier_all();
   };
@@ -632,12 +706,12 @@ void dq_kernel(KernelArgs a) {
 
 template <int D, typename T>
 int launch_d(const BwdArgs& f, hipStream_t st) {
-  const int64_t qrows = (int64_t)f.B * f.N * f.H;
+  const int64_t qrows = (f.cu_q ? (int64_t)f.total_q : (int64_t)f.B * f.N) * f.H;
   if (qrows > 0) {
     constexpr int RPB = 256 / (D / 8);
     const int grid = (int)((qrows + RPB - 1) / RPB);
     hipLaunchKernelGGL((pre_kernel<D, T>), dim3(grid), dim3(256), 0, st, (const T*)f.o, (const T*)f.dout, f.delta,
-                       f.B, f.H, f.N);
+                       f.B, f.H, f.N, f.cu_q ? f.total_q : 0);
   }
   KernelArgs a;
   a.q = f.q; a.k = f.k; a.v = f.v; a.dout = f.dout; a.lse = f.lse; a.delta = f.delta;
@@ -646,6 +720,9 @@ int launch_d(const BwdArgs& f, hipStream_t st) {
   a.Nq = f.N; a.Nk = f.Nk;
   a.n_kblk = (f.Nk + 127) / 128;
   a.n_qblk = (f.N + 127) / 128;
+  a.cu_q = f.cu_q; a.cu_k = f.cu_k;
+  a.total_q = f.total_q; a.total_k = f.total_k;
+  a.win_l = f.win_l; a.win_r = f.win_r;
   a.c = f.scale_log2;
   a.alpha = f.alpha;
   const int kgrid = a.n_kblk * f.B * f.Hkv;

@@ -53,6 +53,10 @@ struct BwdArgs {
   float* delta;
   int B, H, N, d;    // H: query heads, N: query rows per batch entry
   int Hkv, Nk;       // key/value heads (H % Hkv == 0), key rows
+  const int* cu_q;   // packed batches: B + 1 row offsets (N, Nk are maxima)
+  const int* cu_k;
+  int total_q, total_k;
+  int win_l, win_r;  // masked path (causal = 1), as in FwdArgs
   int causal;
   int dtype;
   float alpha;       // alpha, clamped to >= 1e-30 / log2(e)

@@ -241,22 +241,32 @@ int attn_pack_gqa_heuristic(int Hq, int Hkv, int Nq);
 int attn_num_splits_heuristic(int B, int Hq, int Hkv, int Nq, int Nk, int d, int pack_gqa, int num_cus);
 
 /*
- * attn_bwd_ex -- attn_bwd for Hq query heads over Hkv key/value heads and
- * N_q != N_k (dense [B, N, H, d] layouts).
+ * attn_bwd_ex -- attn_bwd generalised like attn_fwd_ex: Hq query heads over
+ * Hkv key/value heads, N_q != N_k, packed variable-length batches and local
+ * (sliding-window) attention.
  *
- *   q, o, dout, dq  [B, Nq, Hq, d];  k, v, dk, dv  [B, Nk, Hkv, d];
- *   lse, delta      float32 [B, Hq, Nq] (lse from attn_fwd_ex, dense).
- *   causal   bottom-right aligned, as in attn_fwd_ex.
+ *   Dense    cu_seqlens_q = cu_seqlens_k = NULL: q, o, dout, dq are
+ *            [B, Nq, Hq, d]; k, v, dk, dv are [B, Nk, Hkv, d]; lse, delta are
+ *            float32 [B, Hq, Nq]; total_q and total_k are ignored.
+ *   Packed   device int32 cu_seqlens_q, cu_seqlens_k of B + 1 row offsets, as
+ *            in attn_fwd_ex: q, o, dout, dq are [total_q, Hq, d]; k, v, dk, dv
+ *            are [total_k, Hkv, d]; lse, delta are float32 [Hq, total_q].
+ *            Nq, Nk are the largest sequence lengths. Rows that no valid
+ *            sequence covers are left unspecified in dq, dk, dv and delta.
+ *   causal, window_left, window_right  the mask of the forward call that
+ *            produced o and lse (same meaning as in attn_fwd_ex).
  *   The gradient of key/value head kh is the sum over the Hq / Hkv query
  *   heads that read it ("FlashAttention-3 on Hopper", section 8.8): each
  *   dK/dV workgroup loops over those heads' query tiles itself, so the sum
- *   takes no atomics and the result is deterministic. Nq = 0 (or Nk = 0)
- *   writes zero dK, dV (or dQ); the pointers of operands of size zero may
- *   then be NULL. Other arguments and errors as attn_bwd.
+ *   takes no atomics and the result is deterministic. Masked keys and
+ *   queries get zero gradients: a sequence with no query rows writes zero
+ *   dK, dV, one with no key rows zero dQ; the pointers of operands of size
+ *   zero may then be NULL. Other arguments and errors as attn_bwd.
  */
 int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                 void* dq, void* dk, void* dv, float* delta, int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                int causal, float alpha, int dtype, void* stream);
+                const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q, int total_k,
+                int causal, int window_left, int window_right, float alpha, int dtype, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */

@@ -155,10 +155,12 @@ def _bwd_ex(**kw):
     lib = ea.load()
     names = ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")
     a = {n: FAKE + i * 0x10000000 for i, n in enumerate(names)}
-    a.update(dict(B=1, Hq=4, Hkv=2, Nq=100, Nk=300, d=128, causal=1, alpha=0.1, dtype=0, stream=None))
+    a.update(dict(B=1, Hq=4, Hkv=2, Nq=100, Nk=300, d=128, cu_q=None, cu_k=None, total_q=0, total_k=0, causal=1,
+                  wl=-1, wr=-1, alpha=0.1, dtype=0, stream=None))
     a.update(kw)
     return lib.attn_bwd_ex(*(a[n] for n in names), a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
-                           a["causal"], a["alpha"], a["dtype"], a["stream"])
+                           a["cu_q"], a["cu_k"], a["total_q"], a["total_k"], a["causal"], a["wl"], a["wr"],
+                           a["alpha"], a["dtype"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -168,6 +170,16 @@ def _bwd_ex(**kw):
     (dict(dv=None), ea.ATTN_ERR_INVALID_ARG, "dv is null"),
     (dict(dk=FAKE + 0x20000000), ea.ATTN_ERR_INVALID_ARG, "dk overlaps v"),
     (dict(causal=5), ea.ATTN_ERR_INVALID_ARG, "causal"),
+    (dict(wl=-2), ea.ATTN_ERR_INVALID_ARG, "window"),
+    (dict(cu_q=FAKE + 0x70000000), ea.ATTN_ERR_INVALID_ARG, "both be given"),
+    (dict(cu_q=FAKE + 0x70000000, cu_k=FAKE + 0x70001000, total_q=-1, total_k=5), ea.ATTN_ERR_INVALID_ARG,
+     "total_q"),
+    (dict(cu_q=FAKE + 0x70000002, cu_k=FAKE + 0x70001000, total_q=100, total_k=300), ea.ATTN_ERR_INVALID_ARG,
+     "4-byte aligned"),
+    # packed: q holds total_q rows, so a dq one row past q's end overlaps nothing
+    # but a dq inside q's 64-row span is caught
+    (dict(cu_q=FAKE + 0x70000000, cu_k=FAKE + 0x70001000, total_q=64, total_k=300, dq=FAKE + 64 * 4 * 128 * 2 - 16),
+     ea.ATTN_ERR_INVALID_ARG, "dq overlaps q"),
 ])
 def test_bwd_ex_rejects_bad_arguments_before_launch(kw, status, msg):
     assert _bwd_ex(**kw) == status
@@ -175,7 +187,8 @@ def test_bwd_ex_rejects_bad_arguments_before_launch(kw, status, msg):
 
 
 def test_bwd_ex_empty_problems_are_no_ops():
-    for kw in (dict(B=0), dict(Hq=0), dict(Nq=0, Nk=0)):
+    for kw in (dict(B=0), dict(Hq=0), dict(Nq=0, Nk=0),
+               dict(cu_q=FAKE + 0x70000000, cu_k=FAKE + 0x70001000, total_q=0, total_k=0)):
         assert _bwd_ex(**kw) == ea.ATTN_OK, kw
 
 

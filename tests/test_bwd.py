@@ -146,3 +146,109 @@ def test_bwd_grouped_heads_deterministic_and_empty_queries(gpu):
     gpu.attn_bwd_ex(q, k, v, q, q, lse, torch.empty_like(q), dk, dv, torch.empty_like(lse), causal=False)
     torch.cuda.synchronize()
     assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+def _blind(nq, nk, causal, win):
+    """Queries that see no key and keys that no query sees, from the mask."""
+    from oracle.attention import causal_mask
+    from oracle.variants import window_mask
+    hidden = window_mask(nq, nk, *win)
+    if causal:
+        hidden = hidden | causal_mask(nq, nk)
+    return hidden.all(axis=1), hidden.all(axis=0)
+
+
+def _grads_ok(grads, refs, tag, blind=None):
+    """Tolerances on dq, dk, dv; with ``blind`` = (rows, keys) boolean masks
+    over the sequence axis (axis -3), those rows of dq and keys of dk, dv are
+    exactly zero."""
+    for i, (name, g, r) in enumerate(zip(("dq", "dk", "dv"), grads, refs)):
+        gv = to_f64(g)
+        assert np.isfinite(gv).all(), (tag, name)
+        e = _rel(gv, r)
+        assert e["rel_max"] <= REL_MAX and e["rel_rms"] <= REL_RMS, (tag, name, e)
+        if blind is not None:
+            m = blind[0] if i == 0 else blind[1]
+            assert np.all(np.take(gv, np.nonzero(m)[0], axis=-3) == 0), (tag, name)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_bwd_local_windows(gpu, d):
+    # sliding windows of the forward (left, right), with and without causal,
+    # on N_q != N_k and grouped heads; every window leaves some keys or rows
+    # outside the band, and (0, 0) a single diagonal
+    import torch
+    from oracle.attention_bwd import attention_backward_gqa
+    from synth_inputs import make_qkv_gqa
+    cases = [(300, 300, True, (40, -1)), (200, 333, True, (100, -1)), (333, 200, False, (17, 25)),
+             (260, 260, False, (2, 1)), (150, 400, False, (-1, 30)), (400, 150, False, (64, -1)),
+             (129, 500, True, (60, -1))]
+    for i, (nq, nk, causal, win) in enumerate(cases):
+        bits, vals = make_qkv_gqa(2, nq, nk, 4, 2, d, seed=d + i)
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda() for b in bits)
+        dbits, dvals = make_dout(2, nq, 4, d, seed=d + i)
+        do = torch.from_numpy(dbits.view(np.int16)).view(torch.bfloat16).cuda()
+        o, lse = gpu.attention_ex(q, k, v, causal=causal, pack_gqa=0, num_splits=1, window=win)
+        grads = gpu.attention_backward_ex(q, k, v, o, lse, do, causal=causal, window=win)
+        torch.cuda.synchronize()
+        refs = attention_backward_gqa(*vals, dvals, None, causal, window=win)
+        _grads_ok(grads, refs, (d, nq, nk, causal, win), _blind(nq, nk, causal, win))
+
+
+def _run_varlen(ea, lens_q, lens_k, Hq, Hkv, d, causal, window=(-1, -1), seed=0):
+    import torch
+    from oracle.attention_bwd import attention_backward_varlen
+    from synth_inputs import make_qkv_gqa
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    tq_, tk_ = int(cu_q[-1]), int(cu_k[-1])
+    bits, vals = make_qkv_gqa(1, tq_, tk_, Hq, Hkv, d, seed=seed)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(b[0]).view(np.int16)).view(torch.bfloat16).cuda() for b in bits)
+    dbits, dvals = make_dout(1, tq_, Hq, d, seed=seed)
+    do = torch.from_numpy(np.ascontiguousarray(dbits[0]).view(np.int16)).view(torch.bfloat16).cuda()
+    tq, tk = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    kw = dict(cu_seqlens_q=tq, cu_seqlens_k=tk, max_seqlen_q=int(max(lens_q)), max_seqlen_k=int(max(lens_k)),
+              window=window)
+    o, lse = ea.attention_ex(q, k, v, causal=causal, pack_gqa=0, num_splits=1, **kw)
+    grads = ea.attention_backward_ex(q, k, v, o, lse, do, causal=causal, **kw)
+    torch.cuda.synchronize()
+    refs = attention_backward_varlen(vals[0][0], vals[1][0], vals[2][0], dvals[0], cu_q, cu_k, None, causal, window)
+    # rows and keys of each sequence that the mask leaves out, over the packed axis
+    rows, keys = [], []
+    for lq, lk in zip(lens_q, lens_k):
+        r, c = _blind(int(lq), int(lk), causal, window)
+        rows.append(r if lk > 0 else np.ones(int(lq), dtype=bool))
+        keys.append(c if lq > 0 else np.ones(int(lk), dtype=bool))
+    blind = (np.concatenate(rows + [np.zeros(0, bool)]), np.concatenate(keys + [np.zeros(0, bool)]))
+    return grads, refs, blind
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_varlen_mixed_lengths(gpu, causal):
+    from synth_inputs import make_seqlens
+    lens_q, _ = make_seqlens(7, 1, 300, seed=1)
+    lens_k, _ = make_seqlens(7, 1, 300, seed=2)
+    lens_q[2] = 0      # a sequence with no query: its dK, dV are zero
+    lens_k[4] = 0      # a sequence with queries but no key: its dQ is zero
+    grads, refs, blind = _run_varlen(gpu, lens_q, lens_k, 4, 2, 128, causal, seed=5)
+    assert blind[0].any() and blind[1].any()
+    _grads_ok(grads, refs, ("varlen", causal), blind)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_bwd_varlen_equal_lengths_and_windows(gpu, d):
+    from synth_inputs import make_seqlens
+    lens, _ = make_seqlens(5, 100, 400, seed=3)
+    for causal, win in ((True, (-1, -1)), (True, (50, -1)), (False, (20, 20))):
+        grads, refs, blind = _run_varlen(gpu, lens, lens, 2, 2, d, causal, win, seed=6 + d)
+        _grads_ok(grads, refs, ("varlen", d, causal, win), blind)
+
+
+def test_bwd_varlen_matches_dense_bitwise(gpu):
+    # one packed sequence is the dense problem: same kernels, same bits
+    import torch
+    lens = np.array([333], dtype=np.int64)
+    grads_v, _, _ = _run_varlen(gpu, lens, lens, 4, 2, 128, True, seed=9)
+    grads_d, _, _ = _run_gqa(gpu, 1, 333, 333, 4, 2, 128, True, seed=9)
+    for a, b in zip(grads_v, grads_d):
+        assert torch.equal(a, b[0])
