@@ -356,7 +356,9 @@ void dkdv_kernel(KernelArgs a) {
   // win_l + win_r, one unsigned compare against a per-tile base. Rows past
   // Nq need no test: their Q and dO rows read as zero (and LSE, D as 0), so
   // p = 1 and dS = 0 add nothing; keys past Nk only reach their own dK/dV
-  // rows, which are not stored.
+  // rows, which are not stored. Nor do rows with LSE = -inf: such a row sees
+  // no key, so the band test is false for every key of a masked call, and
+  // an unmasked call with keys has no such row.
   const uint32_t wspan = (uint32_t)(a.win_l + a.win_r);
   auto band_base = [&](int q0t) ATTN_INLINE { return key - q0t - 4 * h32 - off + a.win_l; };
   auto in_band = [&](int kb, int r) ATTN_INLINE {
@@ -377,8 +379,7 @@ void dkdv_kernel(KernelArgs a) {
     for (int r = 0; r < 16; ++r) {
       const bool ok = !CAUSAL || in_band(kb, r);
       const float lse = l2[r >> 2][r & 3];
-      // a row with LSE = -inf has no keys; its p stays 0
-      const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(s[r], c, -lse * kLog2e)) : 0.f;
+      const float p = ok ? exp2_fast(__builtin_fmaf(s[r], c, -lse * kLog2e)) : 0.f;
       pv[r] = p;
       if constexpr (DO_K) dsv[r] = p * (dp[r] - dl[r >> 2][r & 3]);
     }
@@ -514,7 +515,7 @@ void dkdv_kernel(KernelArgs a) {
           constexpr int r = decltype(r_tag)::value;
           const bool ok = !CAUSAL || in_band(kb, r);
           const float lse = l2c[r >> 2][r & 3];
-          const float p = (ok && lse != -__builtin_inff()) ? exp2_fast(__builtin_fmaf(sc[r], c, -lse * kLog2e)) : 0.f;
+          const float p = ok ? exp2_fast(__builtin_fmaf(sc[r], c, -lse * kLog2e)) : 0.f;
           pv[r] = p;
           dsv[r] = p * (dpc[r] - dlc[r >> 2][r & 3]);
           pin(dsv[r]);
