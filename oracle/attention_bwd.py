@@ -24,7 +24,8 @@ import numpy as np
 
 from .attention import causal_mask
 
-__all__ = ["attention_backward", "attention_backward_head", "attention_backward_gqa", "attention_backward_varlen"]
+__all__ = ["attention_backward", "attention_backward_head", "attention_backward_gqa", "attention_backward_varlen",
+           "attention_backward_sampled"]
 
 
 def attention_backward_head(q, k, v, do, alpha, causal=False, row_chunk=1024, mask=None):
@@ -140,3 +141,69 @@ def attention_backward_varlen(q, k, v, do, cu_q, cu_k, alpha=None, causal=False,
                                             window)
         dq[sq], dk[sk], dv[sk] = gq[0], gk[0], gv[0]
     return dq, dk, dv
+
+
+def attention_backward_sampled(q, k, v, do, alpha, causal=False, rows=(), keys=(), row_chunk=1024):
+    """dQ at the query ``rows`` and dK, dV at the ``keys`` of one head, for
+    sequences too long to materialise the gradients whole.
+
+    q, do are (N_q, d) and k, v (N_k, d). The same formulas as
+    ``attention_backward_head`` (section 7.1 of "FlashAttention-3 on
+    Hopper"), taken one output row at a time:
+
+    * a first pass over row chunks gives every row's LSE and
+      D_i = rowsum(dO_i o O_i) (section 7.1.2), with O = P V;
+    * dQ_i = alpha sum_j P_ij (dP_ij - D_i) K_j for a sampled query i, where
+      P_ij = exp(S_ij - LSE_i) and dP_ij = <dO_i, V_j> (P recomputed from the
+      LSE, section 7.1.3);
+    * dV_j = sum_i P_ij dO_i and dK_j = alpha sum_i P_ij (dP_ij - D_i) Q_i for
+      a sampled key j, from column j of P and dP.
+
+    Causal uses the bottom-right alignment; rows with no visible key have
+    LSE = -inf and P = 0. Returns (dq_rows, dk_keys, dv_keys) as float64
+    arrays of shape (len(rows), d) and (len(keys), d).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    nq, nk = q.shape[0], k.shape[0]
+    off = nk - nq
+    lse = np.full(nq, -np.inf)
+    dvec = np.zeros(nq)
+    for r0 in range(0, nq, row_chunk):
+        r1 = min(nq, r0 + row_chunk)
+        s = alpha * (q[r0:r1] @ k.T)
+        if causal:
+            s = np.where(np.arange(nk)[None, :] > np.arange(r0, r1)[:, None] + off, -np.inf, s)
+        m = s.max(axis=1, keepdims=True) if nk else np.full((r1 - r0, 1), -np.inf)
+        live = np.isfinite(m)
+        e = np.where(live, np.exp(s - np.where(live, m, 0.0)), 0.0)
+        den = e.sum(axis=1, keepdims=True)
+        o = (e / np.where(den > 0, den, 1.0)) @ v
+        lse[r0:r1] = np.where(live[:, 0], m[:, 0] + np.log(np.where(den[:, 0] > 0, den[:, 0], 1.0)), -np.inf)
+        dvec[r0:r1] = np.sum(do[r0:r1] * o, axis=1)
+
+    def p_of(svals, lrow):
+        ok = np.isfinite(svals) & np.isfinite(lrow)
+        return np.where(ok, np.exp(np.where(ok, svals - np.where(np.isfinite(lrow), lrow, 0.0), 0.0)), 0.0)
+
+    dq_rows = np.zeros((len(rows), q.shape[1]))
+    for n, i in enumerate(rows):
+        s = alpha * (k @ q[i])
+        if causal:
+            s = np.where(np.arange(nk) > i + off, -np.inf, s)
+        p = p_of(s, lse[i])
+        ds = p * (v @ do[i] - dvec[i])
+        dq_rows[n] = alpha * (ds @ k)
+    dk_keys = np.zeros((len(keys), k.shape[1]))
+    dv_keys = np.zeros((len(keys), v.shape[1]))
+    for n, j in enumerate(keys):
+        s = alpha * (q @ k[j])
+        if causal:
+            s = np.where(j > np.arange(nq) + off, -np.inf, s)
+        p = p_of(s, lse)
+        ds = p * (do @ v[j] - dvec)
+        dv_keys[n] = p @ do
+        dk_keys[n] = alpha * (ds @ q)
+    return dq_rows, dk_keys, dv_keys

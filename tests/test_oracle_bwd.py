@@ -193,3 +193,29 @@ def test_varlen_backward_is_per_sequence():
         else:
             # a sequence without keys (or queries) has no gradient
             assert np.all(dq[sq] == 0) and np.all(dk[sk] == 0) and np.all(dv[sk] == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(41, 41), (23, 57), (57, 23)])
+def test_sampled_backward_matches_autograd_and_full(causal, nq, nk):
+    # row-by-row dQ and column-by-column dK, dV equal torch float64 autograd
+    # through a plain softmax, and the full oracle, on every row and key
+    from oracle.attention_bwd import attention_backward_head, attention_backward_sampled
+    d = 16
+    q, do = _rand((nq, d), 21), _rand((nq, d), 22)
+    k, v = _rand((nk, d), 23), _rand((nk, d), 24)
+    alpha = 0.3
+    rows, keys = list(range(nq)), list(range(nk))
+    gq, gk, gv = attention_backward_sampled(q, k, v, do, alpha, causal, rows, keys, row_chunk=16)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = alpha * torch.matmul(tq, tk.T.contiguous())
+    if causal:
+        mask = torch.arange(nk)[None, :] > torch.arange(nq)[:, None] + (nk - nq)
+        s = s.masked_fill(mask, float("-inf"))
+    pr = torch.nan_to_num(torch.softmax(s, dim=-1), nan=0.0)   # rows with no key: P = 0
+    (torch.matmul(pr, tv) * torch.tensor(do)).sum().backward()
+    for g, t in ((gq, tq), (gk, tk), (gv, tv)):
+        np.testing.assert_allclose(g, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+    full = attention_backward_head(q, k, v, do, alpha, causal)
+    for g, f in zip((gq, gk, gv), full):
+        np.testing.assert_allclose(g, f, rtol=1e-10, atol=1e-12)
