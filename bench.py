@@ -322,6 +322,8 @@ def main():
                     help="time only the decode workload (8 x 64/8 heads, 8192-key cache) and exit")
     ap.add_argument("--bwd-only", action="store_true",
                     help="time only the backward at the headline shape (causal) and exit")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="time only the FP8 forward at the headline shape (128-row blocks + Hadamard) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -347,6 +349,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.fp8_only:
+        h = HEADLINE
+        r = bench_fp8(ea, h["B"], h["N"], h["H"], h["d"], False, args.steps, args.warmup)
+        print(json.dumps({"fp8": r}), flush=True)
+        return
     if args.bwd_only:
         h = HEADLINE
         r = bench_bwd(ea, h["B"], h["N"], h["H"], h["d"], True, args.steps, args.warmup)

@@ -17,9 +17,10 @@
 // K Q^T so a lane owns one query, online softmax, O^T += V^T P^T -- with the
 // 32x32x64 f8f6f4 MFMA. The descales fold into per-tile scalars: the score
 // scale of tile (i, j) is alpha*log2(e)*dq_i*dk_j, and the running max is
-// kept in those scaled (base-2) units. P is formed as 2^(s - m + 8)
-// (Max_offset = 8 puts the largest probability at 256, inside e4m3's range),
-// rounded to e4m3 and fed to the PV product straight from the score
+// kept in those scaled (base-2) units. P is formed as 2^(s - m + kOff8)
+// against a reference m that may trail the true max by up to kTau8, so the
+// largest probability is at most 2^(kOff8 + kTau8) < 448, inside e4m3's range
+// (the pages' Max_offset, section 6.5), rounded to e4m3 and fed to the PV product straight from the score
 // registers. O~ is kept in units of the current tile's dv: when the tile's dv
 // differs from the previous one the rescale factor includes dv_prev/dv_cur,
 // and the epilogue multiplies by the last dv and divides by l.
@@ -251,10 +252,17 @@ struct Fwd8Args {
   float c;        // alpha * log2(e)
 };
 
-// rescale threshold of the lazy path in base-2 units: with Max_offset 8 a
-// score at most kTau8 above the reference gives p <= 2^8.8 < 448, the e4m3
-// maximum
-constexpr float kTau8 = 0.8f;
+// Exponent offset (the pages' Max_offset) and rescale threshold of the lazy
+// path, in base-2 units: a score at most kTau8 above the reference gives
+// p <= 2^(kOff8 + kTau8) = 2^8.8 < 448, the e4m3 maximum. The pages shift by
+// 8 against the exact running max; with a lazy reference the same bound can
+// be split as 8 + 0.8 or 5 + 3.8. The second split re-does a tile only when
+// one of the wave's rows sees its max rise by 3.8 (a 0.8 rise was common
+// enough that about 30% of tiles were computed twice), and P still reaches up
+// to 2^8.8.
+constexpr float kOff8 = 5.0f;
+constexpr float kTau8 = 3.8f;
+static_assert(kOff8 + kTau8 <= 8.807f, "p must stay below the e4m3 maximum 448");
 
 // Waves per SIMD each kernel is compiled for (its register budget).
 template <int D>
@@ -268,8 +276,8 @@ constexpr int kWaves8 = D == 256 ? 1 : 2;
 //             P_{i+1} from S_{i+1}     (VALU, in the MFMA shadow)
 //
 // Descales. The score scale of tile (i, j) is ct = alpha*log2(e)*dq_i*dk_j and
-// the running max m is kept in those scaled base-2 units; P = 2^(s ct - m + 8)
-// (Max_offset 8). O~ is kept in units of the dv of the last tile added: when
+// the running max m is kept in those scaled base-2 units; P = 2^(s ct - m +
+// kOff8). O~ is kept in units of the dv of the last tile added: when
 // the next tile's V block has another dv, O~ is multiplied by dv_prev/dv_cur
 // together with the rare rescale ("FlashAttention-3 on Hopper", section 6.3:
 // the descale folded into the O rescale). l sums p in float32 (the pages' row
@@ -452,8 +460,8 @@ void fwd8_kernel(Fwd8Args a) {
   auto tile_scalars = [&](auto x_tag) ATTN_INLINE {
     constexpr int X = decltype(x_tag)::value & 1;
     ct = cq * dkt[X];
-    // exponent offset: Max_offset 8 minus the reference
-    ot = (m_run == -__builtin_inff() ? 0.f : -m_run) + 8.0f;
+    // exponent offset: Max_offset minus the reference
+    ot = (m_run == -__builtin_inff() ? 0.f : -m_run) + kOff8;
   };
 
   auto sm_step = [&](auto sb_tag, auto k_tag, auto m_tag, auto max_tag) ATTN_INLINE {
@@ -512,7 +520,7 @@ void fwd8_kernel(Fwd8Args a) {
       const float m_new = __builtin_fmaxf(m_run, mt);
       f = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
       m_run = m_new;
-      ot = (m_new == -__builtin_inff() ? 0.f : -m_new) + 8.0f;
+      ot = (m_new == -__builtin_inff() ? 0.f : -m_new) + kOff8;
       constexpr Sched S1{1};
       For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<SB>{}, k, Int<1>{}, FalseT{}); });
       l_run *= f;
@@ -628,13 +636,13 @@ void fwd8_kernel(Fwd8Args a) {
     iteration(i, Int<0>{}, FalseT{}, FalseT{});
   }
 
-  // finalize: O = O~ dv_cur / l, LSE = (m + log2 l - 8) ln 2
+  // finalize: O = O~ dv_cur / l, LSE = (m + log2 l - kOff8) ln 2
   const float lt = halves_sum(l_run);
   const bool ok = lt > 0.f;
   const float inv = ok ? dv_cur / lt : 0.f;
   if (qi < N) {
     if (h32 == 0) {
-      const float lse = ok ? (m_run + __builtin_amdgcn_logf(lt) - 8.0f) * kLn2 : -__builtin_inff();
+      const float lse = ok ? (m_run + __builtin_amdgcn_logf(lt) - kOff8) * kLn2 : -__builtin_inff();
       a.lse[(int64_t)bh * N + qi] = lse;
     }
     __bf16* orow = a.o + head_off + (int64_t)qi * a.H * D;
