@@ -263,6 +263,12 @@ struct Fwd8Args {
 constexpr float kOff8 = 5.0f;
 constexpr float kTau8 = 3.8f;
 static_assert(kOff8 + kTau8 <= 8.807f, "p must stay below the e4m3 maximum 448");
+// The common path tests the rule on the lane's float32 sum of its tile's p
+// (computed anyway for l): every p is at most that sum, so a sum of at most
+// 2^(kOff8 + kTau8) keeps every p inside e4m3 without a max tree. The tile
+// maximum is then needed only on the rare path.
+constexpr float kPsum8 = 445.0f;  // <= 2^8.8
+static_assert(kPsum8 <= 448.0f, "p must stay below the e4m3 maximum 448");
 
 // Waves per SIMD each kernel is compiled for (its register budget).
 template <int D>
@@ -437,13 +443,14 @@ void fwd8_kernel(Fwd8Args a) {
   };
 
   // ---- online softmax of one tile (32 scores per lane) -----------------------
-  // Conditional rescale ("FlashAttention v1-v4", FA4 section) with threshold
-  // kTau8: p is computed against the current reference while a max tree
-  // checks the rule; a tile that breaks it (always the first) is redone after
-  // its block, and O~ and l are multiplied by rho = 2^(m_old - m_new).
+  // Conditional rescale ("FlashAttention v1-v4", FA4 section): p is computed
+  // against the current reference and the rule is checked on the lane sums
+  // (kPsum8); a tile that breaks it (always the first) is redone after its
+  // block against its maximum, and O~ and l are multiplied by
+  // rho = 2^(m_old - m_new).
   constexpr int NV = 32;
   float fv[NV];
-  float pmx[2], mxv, r32p[2], r32v;
+  float r32p[2], r32v;
   float ct, ot;  // per-tile score scale and exponent offset
   uint32_t pw[8];
   bool need = false;
@@ -452,8 +459,7 @@ void fwd8_kernel(Fwd8Args a) {
     int M;
     constexpr int span() const { return M > 3 ? M - 2 : 1; }
     constexpr int f(int e) const { return (e * span()) / NV; }
-    constexpr int maxs() const { return M / 2 > 0 ? M / 2 : 1; }
-    constexpr int last() const { return f(NV - 1) + 3 > maxs() + 1 ? f(NV - 1) + 3 : maxs() + 1; }
+    constexpr int last() const { return f(NV - 1) + 3; }
   };
 
   // per-tile scalars for the tile with descale slot X
@@ -464,21 +470,14 @@ void fwd8_kernel(Fwd8Args a) {
     ot = (m_run == -__builtin_inff() ? 0.f : -m_run) + kOff8;
   };
 
-  auto sm_step = [&](auto sb_tag, auto k_tag, auto m_tag, auto max_tag) ATTN_INLINE {
+  auto sm_step = [&](auto sb_tag, auto k_tag, auto m_tag, auto check_tag) ATTN_INLINE {
     constexpr int SB = decltype(sb_tag)::value;
     constexpr int K = decltype(k_tag)::value;
     constexpr Sched S{decltype(m_tag)::value};
-    constexpr bool WITH_MAX = decltype(max_tag)::value;
-    constexpr int CH = NV / S.maxs();  // scores per max step
+    constexpr bool CHECK = decltype(check_tag)::value;  // the redo pass does not re-test
     For<0, NV>::run([&](auto e_tag) ATTN_INLINE {
       constexpr int e = decltype(e_tag)::value;
       constexpr int f = S.f(e);
-      if constexpr (WITH_MAX && e % 2 == 0 && e / CH == K) {
-        constexpr int j = ((e % CH) / 2) % 2;
-        const float x0 = s[SB][e / 16][e % 16], x1 = s[SB][(e + 1) / 16][(e + 1) % 16];
-        pmx[j] = (e < 4) ? __builtin_fmaxf(x0, x1) : __builtin_fmaxf(__builtin_fmaxf(pmx[j], x0), x1);
-        pin(pmx[j]);
-      }
       if constexpr (f == K) {
         fv[e] = __builtin_fmaf(s[SB][e / 16][e % 16], ct, ot);
         pin(fv[e]);
@@ -496,14 +495,10 @@ void fwd8_kernel(Fwd8Args a) {
         }
       }
     });
-    if constexpr (WITH_MAX && K == S.maxs()) {
-      mxv = __builtin_fmaxf(pmx[0], pmx[1]);
-      pin(mxv);
-    }
-    if constexpr (WITH_MAX && K == S.maxs() + 1)
-      need = __builtin_amdgcn_ballot_w64(mxv * ct > m_run + kTau8 || m_run == -__builtin_inff()) != 0;
     if constexpr (K == S.last()) {
       r32v = r32p[0] + r32p[1];
+      if constexpr (CHECK)
+        need = __builtin_amdgcn_ballot_w64(!(r32v <= kPsum8) || m_run == -__builtin_inff()) != 0;
       i32x8 w;
 #pragma unroll
       for (int g = 0; g < 8; ++g) w[g] = (int)pw[g];
@@ -516,7 +511,10 @@ void fwd8_kernel(Fwd8Args a) {
     constexpr int SB = decltype(sb_tag)::value;
     float f = 1.f;
     if (need) {
-      const float mt = halves_max(mxv) * ct;
+      float mx = s[SB][0][0];
+#pragma unroll
+      for (int e = 1; e < NV; ++e) mx = __builtin_fmaxf(mx, s[SB][e / 16][e % 16]);
+      const float mt = halves_max(mx) * ct;
       const float m_new = __builtin_fmaxf(m_run, mt);
       f = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
       m_run = m_new;
@@ -525,13 +523,16 @@ void fwd8_kernel(Fwd8Args a) {
       For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<SB>{}, k, Int<1>{}, FalseT{}); });
       l_run *= f;
     }
-    const float dvr = dv_cur / dvt[SB];
-    dv_cur = dvt[SB];
-    if (need || dvr != 1.f) {
-      f *= dvr;
+    // O~ moves to this tile's dv units only when its V block has another
+    // descale (every other tile with 128-row blocks); the division stays off
+    // the tiles that share the previous block's dv
+    const bool chg = dvt[SB] != dv_cur;
+    if (need || chg) {
+      if (chg) f *= dv_cur / dvt[SB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= f;
     }
+    dv_cur = dvt[SB];
     l_run += r32v;
   };
 
