@@ -125,12 +125,31 @@ constexpr bool kPipeDkdv = D == 128;
 template <int D>
 constexpr int kWavesDq = D == 256 ? 1 : 2;
 
-// Per-lane LDS offsets shared by both kernels for 32-row tiles stored with the
-// K-style swizzle (they are read row-wise as MFMA A operands and, for the
-// transposed operands, through ds_read_b64_tr_b16).
+// XOR swizzle of the 16-byte chunk index of row r of a backward tile. The
+// tiles are read two ways. Row-wise (ds_read_b128, the A operand of S or
+// dP), 16 lanes read 16 consecutive rows at one logical chunk, so those rows
+// must land on 16 different 16-byte bank groups. Transposed
+// (ds_read_b64_tr_b16, the A operand of dV, dK or dQ), 32 lanes read 4
+// consecutive rows (4h..4h+3) of an aligned 4-chunk quad, so the 4 rows must
+// land in different quads of the 256-byte bank line. A plain r & 15 XOR only
+// permutes chunks inside a quad, which put all 4 rows of a transposed read
+// on the same banks. At d >= 128 (a row spans whole lines) the low two row
+// bits move the quad and the next two bits permute inside it. At d = 64 two
+// rows share a line, so the row parity already separates them; row bit 1
+// moves the quad and row bits 2-3 permute inside it. Both are bijections
+// over 16 consecutive rows and have period 16, which the copy offsets assume.
 template <int D>
+__device__ __forceinline__ int swz_b(int r) {
+  return D == 64 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
+
+// Per-lane LDS offsets shared by both kernels for 32-row tiles stored with the
+// swz_b swizzle (they are read row-wise as MFMA A operands and, for the
+// transposed operands, through ds_read_b64_tr_b16).
+template <int D, bool SWB = true>
 struct TileOffsets {
   typedef Geo<D, 1> G;
+  static __device__ __forceinline__ int swz(int r) { return SWB ? swz_b<D>(r) : swz_k<D>(r); }
   static constexpr int KC = D / 16;
   static constexpr int KCL = KC < 8 ? KC : 8;
   static constexpr int DB = D / 32;
@@ -145,10 +164,10 @@ struct TileOffsets {
     for (int t = 0; t < KGP; ++t) {
       const int r = (wave + 4 * t) * G::RPS + lane / G::CPR;
       const int pc = lane % G::CPR;
-      cg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * 4 * G::RPS * RS;
+      cg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz(r)) << 4) - (uint32_t)t * 4 * G::RPS * RS;
     }
 #pragma unroll
-    for (int i = 0; i < KCL; ++i) rofs[i] = l32 * G::ROWB + (((2 * i + h32) ^ swz_k<D>(l32)) << 4);
+    for (int i = 0; i < KCL; ++i) rofs[i] = l32 * G::ROWB + (((2 * i + h32) ^ swz(l32)) << 4);
     // 16-lane group g = lane/16, piece p = lane%16: row 4*h32 + p/4 (+8 for the
     // second read), dims db*32 + 16*(g%2) + 4*(p%4)
     const int p = lane & 15, dh = (lane >> 4) & 1;
@@ -156,35 +175,35 @@ struct TileOffsets {
 #pragma unroll
     for (int i = 0; i < DBL; ++i) {
       const int ch = 4 * i + 2 * dh + ((p & 3) >> 1);
-      tlo[i] = r0 * G::ROWB + ((ch ^ swz_k<D>(r0)) << 4) + 8 * (p & 1);
-      thi[i] = (r0 + 8) * G::ROWB + ((ch ^ swz_k<D>(r0 + 8)) << 4) + 8 * (p & 1);
+      tlo[i] = r0 * G::ROWB + ((ch ^ swz(r0)) << 4) + 8 * (p & 1);
+      thi[i] = (r0 + 8) * G::ROWB + ((ch ^ swz(r0 + 8)) << 4) + 8 * (p & 1);
     }
   }
 };
 
-// Copy 32 rows starting at row0 of one head into an LDS tile (K-style
+// Copy 32 rows starting at row0 of one head into an LDS tile (swz_b
 // swizzle); extra is a byte offset added to every row (the head within a
 // group of heads that share the buffer resource).
-template <int D>
-__device__ __forceinline__ void copy_tile(const TileOffsets<D>& to, const __amdgpu_buffer_rsrc_t& rs, char* dst,
+template <int D, bool SWB>
+__device__ __forceinline__ void copy_tile(const TileOffsets<D, SWB>& to, const __amdgpu_buffer_rsrc_t& rs, char* dst,
                                           int wave, int row0, uint32_t RS, uint32_t extra = 0) {
   typedef Geo<D, 1> G;
   const uint32_t base = (uint32_t)row0 * RS + extra;
 #pragma unroll
   for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
-    const uint32_t voff = to.cg[(t & 1) % TileOffsets<D>::KGP] + (base + (uint32_t)t * 4 * G::RPS * RS);
+    const uint32_t voff = to.cg[(t & 1) % TileOffsets<D, SWB>::KGP] + (base + (uint32_t)t * 4 * G::RPS * RS);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + 4 * t) * 1024), 16, voff, 0, 0, 0);
   }
 }
 
 // A operand of row-read tile rows (32 rows x 16 dims, step kc)
-template <int D, typename T>
-__device__ __forceinline__ typename Elt<T>::v8 row_op(const TileOffsets<D>& to, const char* tile, int kc) {
+template <int D, typename T, bool SWB>
+__device__ __forceinline__ typename Elt<T>::v8 row_op(const TileOffsets<D, SWB>& to, const char* tile, int kc) {
   return *(const typename Elt<T>::v8*)(tile + (kc / 8) * 256 + to.rofs[kc % 8]);
 }
 // A operand of the transposed tile: 32 dims (block db) x 16 rows (chunk ks)
-template <int D, typename T>
-__device__ __forceinline__ typename Elt<T>::v8 tr_op(const TileOffsets<D>& to, const char* tile, int db, int ks) {
+template <int D, typename T, bool SWB>
+__device__ __forceinline__ typename Elt<T>::v8 tr_op(const TileOffsets<D, SWB>& to, const char* tile, int db, int ks) {
   typedef Elt<T> E;
   const LDS_AS char* base = (const LDS_AS char*)tile + 16 * ks * Geo<D, 1>::ROWB + (db / 4) * 256;
   const typename E::v4 lo = E::tr_read(base + to.tlo[db % 4]);
@@ -513,8 +532,11 @@ void dkdv_kernel(KernelArgs a) {
         // p and dS of the scores assigned to this step
         For<(m * 16) / NM, ((m + 1) * 16) / NM>::run([&](auto r_tag) ATTN_INLINE {
           constexpr int r = decltype(r_tag)::value;
-          const bool ok = !CAUSAL || in_band(kb, r);
           const float lse = l2c[r >> 2][r & 3];
+          // unmasked: the LSE = -inf select never fires (no row is without
+          // keys), but without it the register allocation of this
+          // instantiation spills
+          const bool ok = CAUSAL ? in_band(kb, r) : lse != -__builtin_inff();
           const float p = ok ? exp2_fast(__builtin_fmaf(sc[r], c, -lse * kLog2e)) : 0.f;
           pv[r] = p;
           dsv[r] = p * (dpc[r] - dlc[r >> 2][r & 3]);
