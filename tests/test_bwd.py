@@ -195,24 +195,25 @@ def test_bwd_local_windows(gpu, d):
         _grads_ok(grads, refs, (d, nq, nk, causal, win), _blind(nq, nk, causal, win))
 
 
-def _run_varlen(ea, lens_q, lens_k, Hq, Hkv, d, causal, window=(-1, -1), seed=0):
+def _run_varlen(ea, lens_q, lens_k, Hq, Hkv, d, causal, window=(-1, -1), seed=0, dtype="bf16", alpha=None):
     import torch
     from oracle.attention_bwd import attention_backward_varlen
     from synth_inputs import make_qkv_gqa
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
     tq_, tk_ = int(cu_q[-1]), int(cu_k[-1])
-    bits, vals = make_qkv_gqa(1, tq_, tk_, Hq, Hkv, d, seed=seed)
-    q, k, v = (torch.from_numpy(np.ascontiguousarray(b[0]).view(np.int16)).view(torch.bfloat16).cuda() for b in bits)
-    dbits, dvals = make_dout(1, tq_, Hq, d, seed=seed)
-    do = torch.from_numpy(np.ascontiguousarray(dbits[0]).view(np.int16)).view(torch.bfloat16).cuda()
+    bits, vals = make_qkv_gqa(1, tq_, tk_, Hq, Hkv, d, seed=seed, dtype=dtype)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(b[0]).view(np.int16)).view(tdt).cuda() for b in bits)
+    dbits, dvals = make_dout(1, tq_, Hq, d, seed=seed, dtype=dtype)
+    do = torch.from_numpy(np.ascontiguousarray(dbits[0]).view(np.int16)).view(tdt).cuda()
     tq, tk = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
     kw = dict(cu_seqlens_q=tq, cu_seqlens_k=tk, max_seqlen_q=int(max(lens_q)), max_seqlen_k=int(max(lens_k)),
               window=window)
-    o, lse = ea.attention_ex(q, k, v, causal=causal, pack_gqa=0, num_splits=1, **kw)
-    grads = ea.attention_backward_ex(q, k, v, o, lse, do, causal=causal, **kw)
+    o, lse = ea.attention_ex(q, k, v, causal=causal, alpha=alpha, pack_gqa=0, num_splits=1, **kw)
+    grads = ea.attention_backward_ex(q, k, v, o, lse, do, causal=causal, alpha=alpha, **kw)
     torch.cuda.synchronize()
-    refs = attention_backward_varlen(vals[0][0], vals[1][0], vals[2][0], dvals[0], cu_q, cu_k, None, causal, window)
+    refs = attention_backward_varlen(vals[0][0], vals[1][0], vals[2][0], dvals[0], cu_q, cu_k, alpha, causal, window)
     # rows and keys of each sequence that the mask leaves out, over the packed axis
     rows, keys = [], []
     for lq, lk in zip(lens_q, lens_k):
@@ -273,3 +274,16 @@ def test_bwd_full_size_sampled(gpu, causal):
             assert np.isfinite(g).all(), (b, h, name)
             e = _rel(g, r)
             assert e["rel_max"] <= REL_MAX and e["rel_rms"] <= REL_RMS, (causal, b, h, name, e)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_bwd_f16_grouped_varlen_window_alpha(gpu, d):
+    # f16 inputs, 6 query heads over 2 KV heads, packed sequences of unequal
+    # query and key lengths, a causal sliding window and a non-default alpha,
+    # all in one call
+    from synth_inputs import make_seqlens
+    lens_q, _ = make_seqlens(4, 30, 260, seed=20 + d)
+    lens_k, _ = make_seqlens(4, 30, 260, seed=30 + d)
+    grads, refs, blind = _run_varlen(gpu, lens_q, lens_k, 6, 2, d, True, (70, -1), seed=40 + d, dtype="f16",
+                                     alpha=0.2)
+    _grads_ok(grads, refs, ("f16", d), blind)
