@@ -284,6 +284,12 @@ void dkdv_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(1024))) char obuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf1[G::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf2[PIPE ? G::TILE : 16];
+  // pipelined kernel: LSE (floats 0..63) and D (64..127) of each slot's 32
+  // query rows, copied by DMA with the tile (rows r and r + 32 hold the same
+  // value); every lane of a half-wave reads the same 16 rows back
+  __shared__ __attribute__((aligned(16))) float rows0[PIPE ? 128 : 4];
+  __shared__ __attribute__((aligned(16))) float rows1[PIPE ? 128 : 4];
+  __shared__ __attribute__((aligned(16))) float rows2[PIPE ? 128 : 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -463,8 +469,11 @@ void dkdv_kernel(KernelArgs a) {
     // the VALU work of tile u (p and dS), then the dV and dK products of tile
     // u. Q/dO tiles rotate through three LDS slots: step u reads tiles u
     // (transposed) and u+1 (rows) while tile u+2 is copied in.
-    f32x4 l2c[4], dlc[4], l2n[4], dln[4];
     f32x16 sc = f32x16{}, dpc = f32x16{};
+    auto slot_r = [&](auto j) ATTN_INLINE -> float* {
+      constexpr int J = decltype(j)::value % 3;
+      return J == 0 ? rows0 : J == 1 ? rows1 : rows2;
+    };
     auto slot_q = [&](auto j) ATTN_INLINE -> char* {
       constexpr int J = decltype(j)::value % 3;
       return J == 0 ? qbuf0 : J == 1 ? qbuf1 : qbuf2;
@@ -473,19 +482,21 @@ void dkdv_kernel(KernelArgs a) {
       constexpr int J = decltype(j)::value % 3;
       return J == 0 ? obuf0 : J == 1 ? obuf1 : obuf2;
     };
-    // copy tile u (Q and dO rows of its head) into slot st
-    auto copy_u = [&](int u, char* qd, char* od) ATTN_INLINE {
+    // copy tile u (Q and dO rows of its head, and their LSE and D) into a slot;
+    // rows past Nq read as 0 (harmless: their Q and dO rows are zero too)
+    auto copy_u = [&](int u, char* qd, char* od, float* rd_) ATTN_INLINE {
       int q0t, j;
       tile_of(u, q0t, j);
       copy_tile<D>(to, rq, qd, wave, q0t, RSQ, (uint32_t)j * D * 2);
       copy_tile<D>(to, ro, od, wave, q0t, RSQ, (uint32_t)j * D * 2);
+      const int row = q0t + l32;
+      const uint32_t lo = row < Nq ? ((uint32_t)j * l_hs + (uint32_t)row) * 4 : 0xffffffffu;
+      if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)rd_, 4, lo, 0, 0, 0);
+      if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void*)(rd_ + 64), 4, lo, 0, 0, 0);
     };
     if (nu > 0) {
-      copy_u(0, qbuf0, obuf0);
-      if (nu > 1) copy_u(1, qbuf1, obuf1);
-      int q0t, j;
-      tile_of(0, q0t, j);
-      load_rows(q0t, j, l2c, dlc);
+      copy_u(0, qbuf0, obuf0, rows0);
+      if (nu > 1) copy_u(1, qbuf1, obuf1, rows1);
       wait_vmcnt<0>();
       barrier_all();
 #pragma unroll
@@ -499,11 +510,16 @@ void dkdv_kernel(KernelArgs a) {
       constexpr bool NEXT = decltype(next_tag)::value;  // tile u+1 exists
       const char* qn = slot_q(Int<J + 1>{});
       const char* on = slot_o(Int<J + 1>{});
-      if (u + 2 < nu) copy_u(u + 2, slot_q(Int<J + 2>{}), slot_o(Int<J + 2>{}));
-      if constexpr (NEXT) {
-        int q0n, jn;
-        tile_of(u + 1, q0n, jn);
-        load_rows(q0n, jn, l2n, dln);
+      if (u + 2 < nu) copy_u(u + 2, slot_q(Int<J + 2>{}), slot_o(Int<J + 2>{}), slot_r(Int<J + 2>{}));
+      // LSE and D of this tile's rows 8g + 4*h32 + 0..3, from its slot
+      f32x4 l2c[4], dlc[4];
+      {
+        const float* rw = slot_r(Int<J>{});
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          l2c[g] = *(const f32x4*)(rw + 8 * g + 4 * h32);
+          dlc[g] = *(const f32x4*)(rw + 64 + 8 * g + 4 * h32);
+        }
       }
       f32x16 sn = f32x16{}, dpn = f32x16{};
       float pv[16], dsv[16];
@@ -560,11 +576,6 @@ void dkdv_kernel(KernelArgs a) {
       barrier_all();
       sc = sn;
       dpc = dpn;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l2c[g] = l2n[g];
-        dlc[g] = dln[g];
-      }
     };
     // unrolled by three so every slot is a compile-time object
     int u = 0;
