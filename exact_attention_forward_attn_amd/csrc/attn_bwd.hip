@@ -284,11 +284,11 @@ void dkdv_kernel(KernelArgs a) {
   __shared__ __attribute__((aligned(1024))) char obuf0[G::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf1[G::TILE];
   __shared__ __attribute__((aligned(1024))) char obuf2[PIPE ? G::TILE : 16];
-  // pipelined kernel: LSE (floats 0..63) and D (64..127) of each slot's 32
-  // query rows, copied by DMA with the tile (rows r and r + 32 hold the same
-  // value); every lane of a half-wave reads the same 16 rows back
-  __shared__ __attribute__((aligned(16))) float rows0[PIPE ? 128 : 4];
-  __shared__ __attribute__((aligned(16))) float rows1[PIPE ? 128 : 4];
+  // LSE (floats 0..63) and D (64..127) of each slot's 32 query rows, copied
+  // by DMA with the tile (rows r and r + 32 hold the same value); every lane
+  // of a half-wave reads the same 16 rows back
+  __shared__ __attribute__((aligned(16))) float rows0[128];
+  __shared__ __attribute__((aligned(16))) float rows1[128];
   __shared__ __attribute__((aligned(16))) float rows2[PIPE ? 128 : 4];
 
   const int lane = threadIdx.x & 63;
@@ -342,21 +342,6 @@ void dkdv_kernel(KernelArgs a) {
     if constexpr (DO_V) dvt[db] = f32x16{};
   }
   const float c = a.c;
-
-  // LSE and D of the 16 query rows a lane holds in a tile of head j of the
-  // group: rows 8g + 4*h32 + 0..3 of the tile for g = 0..3 (dword loads;
-  // rows past Nq are masked, and past the group's end read as 0)
-  auto load_rows = [&](int q0t, int j, f32x4 (&l2)[4], f32x4 (&dl)[4]) ATTN_INLINE {
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = q0t + 8 * g + 4 * h32 + e;
-        const uint32_t lo = row < Nq ? ((uint32_t)j * l_hs + row) * 4 : 0xffffffffu;
-        l2[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, lo, 0, 0));
-        dl[g][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, lo, 0, 0));
-      }
-  };
 
   // query tiles of one head: in the masked instantiation query n sees key k
   // iff n + off - win_l <= k <= n + off + win_r, so only the tiles of rows
@@ -420,14 +405,30 @@ void dkdv_kernel(KernelArgs a) {
       }
   };
 
+  // copy tile u (Q and dO rows of its head, and their LSE and D) into a slot;
+  // rows past Nq read as 0 (harmless: their Q and dO rows are zero too)
+  auto copy_u = [&](int u, char* qd, char* od, float* rd_) ATTN_INLINE {
+    int q0t, j;
+    tile_of(u, q0t, j);
+    copy_tile<D>(to, rq, qd, wave, q0t, RSQ, (uint32_t)j * D * 2);
+    copy_tile<D>(to, ro, od, wave, q0t, RSQ, (uint32_t)j * D * 2);
+    const int row = q0t + l32;
+    const uint32_t lo = row < Nq ? ((uint32_t)j * l_hs + (uint32_t)row) * 4 : 0xffffffffu;
+    if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)rd_, 4, lo, 0, 0, 0);
+    if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void*)(rd_ + 64), 4, lo, 0, 0, 0);
+  };
+  // LSE and D of rows 8g + 4*h32 + 0..3 of the tile in a slot
+  auto read_rows = [&](const float* rw, f32x4 (&l2)[4], f32x4 (&dl)[4]) ATTN_INLINE {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      l2[g] = *(const f32x4*)(rw + 8 * g + 4 * h32);
+      dl[g] = *(const f32x4*)(rw + 64 + 8 * g + 4 * h32);
+    }
+  };
+
   if constexpr (!PIPE) {
-    f32x4 l2c[4], dlc[4], l2n[4], dln[4];
     if (nu > 0) {
-      int q0t, j;
-      tile_of(0, q0t, j);
-      copy_tile<D>(to, rq, qbuf0, wave, q0t, RSQ, (uint32_t)j * D * 2);
-      copy_tile<D>(to, ro, obuf0, wave, q0t, RSQ, (uint32_t)j * D * 2);
-      load_rows(q0t, j, l2c, dlc);
+      copy_u(0, qbuf0, obuf0, rows0);
       wait_vmcnt<0>();
       barrier_all();
     }
@@ -439,23 +440,14 @@ void dkdv_kernel(KernelArgs a) {
       char* ocur = J ? obuf1 : obuf0;
       char* qnxt = J ? qbuf0 : qbuf1;
       char* onxt = J ? obuf0 : obuf1;
-      if (u + 1 < nu) {
-        int q0n, jn;
-        tile_of(u + 1, q0n, jn);
-        copy_tile<D>(to, rq, qnxt, wave, q0n, RSQ, (uint32_t)jn * D * 2);
-        copy_tile<D>(to, ro, onxt, wave, q0n, RSQ, (uint32_t)jn * D * 2);
-        load_rows(q0n, jn, l2n, dln);
-      }
+      if (u + 1 < nu) copy_u(u + 1, qnxt, onxt, J ? rows0 : rows1);
+      f32x4 l2c[4], dlc[4];
+      read_rows(J ? rows1 : rows0, l2c, dlc);
       int q0t, j;
       tile_of(u, q0t, j);
       compute(qcur, ocur, q0t, l2c, dlc);
       wait_vmcnt<0>();
       barrier_all();
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l2c[g] = l2n[g];
-        dlc[g] = dln[g];
-      }
     };
     int u = 0;
     for (; u + 1 < nu; u += 2) {
@@ -482,18 +474,6 @@ void dkdv_kernel(KernelArgs a) {
       constexpr int J = decltype(j)::value % 3;
       return J == 0 ? obuf0 : J == 1 ? obuf1 : obuf2;
     };
-    // copy tile u (Q and dO rows of its head, and their LSE and D) into a slot;
-    // rows past Nq read as 0 (harmless: their Q and dO rows are zero too)
-    auto copy_u = [&](int u, char* qd, char* od, float* rd_) ATTN_INLINE {
-      int q0t, j;
-      tile_of(u, q0t, j);
-      copy_tile<D>(to, rq, qd, wave, q0t, RSQ, (uint32_t)j * D * 2);
-      copy_tile<D>(to, ro, od, wave, q0t, RSQ, (uint32_t)j * D * 2);
-      const int row = q0t + l32;
-      const uint32_t lo = row < Nq ? ((uint32_t)j * l_hs + (uint32_t)row) * 4 : 0xffffffffu;
-      if (wave == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)rd_, 4, lo, 0, 0, 0);
-      if (wave == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (LDS_AS void*)(rd_ + 64), 4, lo, 0, 0, 0);
-    };
     if (nu > 0) {
       copy_u(0, qbuf0, obuf0, rows0);
       if (nu > 1) copy_u(1, qbuf1, obuf1, rows1);
@@ -511,16 +491,9 @@ void dkdv_kernel(KernelArgs a) {
       const char* qn = slot_q(Int<J + 1>{});
       const char* on = slot_o(Int<J + 1>{});
       if (u + 2 < nu) copy_u(u + 2, slot_q(Int<J + 2>{}), slot_o(Int<J + 2>{}), slot_r(Int<J + 2>{}));
-      // LSE and D of this tile's rows 8g + 4*h32 + 0..3, from its slot
+      // LSE and D of this tile's rows, from its slot
       f32x4 l2c[4], dlc[4];
-      {
-        const float* rw = slot_r(Int<J>{});
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          l2c[g] = *(const f32x4*)(rw + 8 * g + 4 * h32);
-          dlc[g] = *(const f32x4*)(rw + 64 + 8 * g + 4 * h32);
-        }
-      }
+      read_rows(slot_r(Int<J>{}), l2c, dlc);
       f32x16 sn = f32x16{}, dpn = f32x16{};
       float pv[16], dsv[16];
       int q0t, jcur;
