@@ -628,7 +628,8 @@ void dq_kernel(KernelArgs a) {
   const float lse = qi < Nq ? a.lse[li] : -__builtin_inff();
   const float dl = qi < Nq ? a.delta[li] : 0.f;
   const bool live = lse != -__builtin_inff();
-  const float l2 = live ? lse * kLog2e : 0.f;
+  // a row past Nq or with LSE = -inf gets l2 = +inf: p = 2^(s c - inf) = 0
+  const float l2 = live ? lse * kLog2e : __builtin_inff();
 
   f32x16 dqt[DB];
 #pragma unroll
@@ -645,16 +646,23 @@ void dq_kernel(KernelArgs a) {
   const int tk0 = kv_lo / 32;
   const int nkt = kv_end > 32 * tk0 ? (kv_end - 32 * tk0 + 31) / 32 : 0;
 
-  auto compute = [&](const char* kt, const char* vt, int kv0) ATTN_INLINE {
+  // MASK: the tile holds keys past Nk or outside some row's band; without
+  // it every key of the tile is seen by every row of the wave
+  auto compute = [&](const char* kt, const char* vt, int kv0, auto mask_tag) ATTN_INLINE {
+    constexpr bool MASK = decltype(mask_tag)::value;
     // keys this lane's row sees, relative to the lane's first key of the tile
     // (kv0 + 4*h32); a row past Nq or with LSE = -inf sees none
-    const int base = kv0 + 4 * h32;
-    int lo = CAUSAL ? qi + off - a.win_l - base : -base;
-    const int hi = min(Nk - 1, CAUSAL ? qi + off + a.win_r : Nk) - base;
-    uint32_t span = (uint32_t)(hi - lo);
-    if (!live || hi < lo) {
-      lo = 1 << 30;
-      span = 0;
+    int lo = 0;
+    uint32_t span = 0;
+    if constexpr (MASK) {
+      const int base = kv0 + 4 * h32;
+      lo = CAUSAL ? qi + off - a.win_l - base : -base;
+      const int hi = min(Nk - 1, CAUSAL ? qi + off + a.win_r : Nk) - base;
+      span = (uint32_t)(hi - lo);
+      if (!live || hi < lo) {
+        lo = 1 << 30;
+        span = 0;
+      }
     }
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -668,7 +676,7 @@ void dq_kernel(KernelArgs a) {
       // lies in [0, span] (unsigned); the span also stops at Nk, since a
       // zero-filled key row past Nk could make p overflow
       const int cr = 8 * (r >> 2) + (r & 3);
-      const bool ok = (uint32_t)(cr - lo) <= span;
+      const bool ok = !MASK || (uint32_t)(cr - lo) <= span;
       const float p = ok ? exp2_fast(__builtin_fmaf(s[r], c, -l2)) : 0.f;
       dsv[r] = p * (dp[r] - dl);
     }
@@ -696,7 +704,14 @@ void dq_kernel(KernelArgs a) {
       copy_tile<D>(to, rk, knxt, wave, 32 * (tk0 + t + 1), RSK);
       copy_tile<D>(to, rv, vnxt, wave, 32 * (tk0 + t + 1), RSK);
     }
-    compute(kcur, vcur, 32 * (tk0 + t));
+    const int kv0 = 32 * (tk0 + t);
+    const int qw0 = q0 + 32 * wave;  // the wave's first query row
+    const bool full = kv0 + 32 <= Nk && (!CAUSAL || (kv0 + 31 <= qw0 + off + a.win_r &&
+                                                     kv0 >= qw0 + 31 + off - a.win_l));
+    if (full)
+      compute(kcur, vcur, kv0, FalseT{});
+    else
+      compute(kcur, vcur, kv0, TrueT{});
     wait_vmcnt<0>();
     barrier_all();
   };
