@@ -215,6 +215,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   const void* ptrs[5] = {q, k, v, o, lse};
   const char* names[5] = {"q", "k", "v", "o", "lse"};
   for (int i = 0; i < 5; ++i) {
+    // k and v hold no rows when no sequence has keys (every row then gets
+    // O = 0, LSE = -inf) and may be null
+    if ((i == 1 || i == 2) && total_k == 0) continue;
     if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
     if (!aligned16(ptrs[i])) return fail(ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
   }

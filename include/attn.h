@@ -211,7 +211,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  *            attn_splitkv_workspace_bytes(num_splits, total_q, Hq, d) bytes,
  *            16-byte aligned, not overlapping any other argument; unused (may
  *            be NULL) when one range is used.
- *   Other arguments, errors and the rounding as attn_fwd. Empty problems
+ *   k and v may be NULL when no sequence has keys (total_k = 0, or Nk = 0
+ *   for dense inputs). Other arguments, errors and the rounding as attn_fwd.
+ *   Empty problems
  *   (B, Hq, Nq or total_q = 0) are no-ops; Nk = 0 (or an empty key sequence)
  *   gives O = 0 and LSE = -inf for its rows.
  */

@@ -1,0 +1,141 @@
+"""Randomised parity sweep of the generalised forward and backward.
+
+A seeded generator draws configurations that combine every option of
+attn_fwd_ex / attn_bwd_ex at once: dtype, head dim, grouped heads, N_q != N_k,
+dense or packed batches (with empty sequences), causal and sliding windows,
+alpha and the number of key ranges. Each one runs the library's forward and
+backward and compares them with the float64 oracle under the bounds of the
+dedicated tests: forward RMSE <= 3e-3 and LSE within 1e-3; gradients within
+2e-2 of their largest entry (max) and 1e-2 (rms). The forward's max |O - O_ref|
+<= 1e-2 is scaled by max(1, max |O_ref|). O and P are rounded to 16 bits, a
+relative error of up to 2^-9 each, and rows that attend to a few keys
+(N_k = 4, or a sharp alpha) have |O| up to ~4. There the rounding alone
+reaches ~1e-2, while the benchmark shapes keep |O| < 1.
+Rows that see no key and keys that no row sees must come out exactly zero.
+The shapes are small (the oracle finishes each in well under a second) but
+span several tiles and ragged tails.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+from gpu_util import errors, to_f64
+from oracle.attention import causal_mask
+from oracle.attention_bwd import attention_backward_gqa, attention_backward_varlen
+from oracle.variants import attention_gqa, attention_varlen, window_mask
+from synth_inputs import make_dout, make_qkv_gqa
+
+pytestmark = pytest.mark.gpu
+
+N_CONFIGS = 60
+
+
+def _draw(i):
+    r = np.random.default_rng([2024, i])
+    d = int(r.choice([64, 128, 256]))
+    hkv = int(r.choice([1, 2, 3]))
+    g = int(r.choice([1, 2, 4]))
+    cfg = dict(
+        d=d, hq=hkv * g, hkv=hkv, dtype=str(r.choice(["bf16", "f16"])),
+        packed=bool(r.random() < 0.4), causal=bool(r.random() < 0.5),
+        alpha=None if r.random() < 0.6 else float(r.uniform(0.02, 0.3)),
+        splits=int(r.choice([1, 1, 2, 5])), seed=int(r.integers(0, 10 ** 6)),
+    )
+    # widths from 1: with a single visible key per row dS is 0 in exact
+    # arithmetic and a gradient's size says nothing
+    wl = -1 if r.random() < 0.6 else int(r.integers(1, 150))
+    wr = -1 if (cfg["causal"] or r.random() < 0.6) else int(r.integers(1, 150))
+    cfg["window"] = (wl, wr)
+    if cfg["packed"]:
+        nb = int(r.integers(1, 5))
+        lq = r.integers(1, 260, nb)
+        lk = r.integers(1, 260, nb)
+        if nb > 1 and r.random() < 0.5:
+            lq[r.integers(1, nb)] = 0  # a sequence without queries (sequence 0 keeps some)
+        if r.random() < 0.5:
+            lk[r.integers(0, nb)] = 0  # a sequence without keys
+        cfg.update(lens_q=lq.astype(np.int64), lens_k=lk.astype(np.int64))
+    else:
+        cfg.update(B=int(r.integers(1, 3)), nq=int(r.integers(1, 300)), nk=int(r.integers(1, 300)))
+    return cfg
+
+
+def _blind(nq, nk, causal, win):
+    hidden = window_mask(nq, nk, *win)
+    if causal:
+        hidden = hidden | causal_mask(nq, nk)
+    return hidden.all(axis=1), hidden.all(axis=0)
+
+
+def _grad_check(g, ref, blind, tag):
+    gv = to_f64(g)
+    assert gv.shape == ref.shape, tag
+    if ref.size == 0:  # no keys at all: dK and dV are empty
+        return
+    assert np.isfinite(gv).all(), tag
+    scale_max = float(np.abs(ref).max()) or 1.0
+    scale_rms = float(math.sqrt(np.mean(ref ** 2))) or 1.0
+    diff = gv - ref
+    assert float(np.abs(diff).max()) <= 2e-2 * scale_max, (tag, float(np.abs(diff).max()) / scale_max)
+    assert float(math.sqrt(np.mean(diff ** 2))) <= 1e-2 * scale_rms, tag
+    idx = np.nonzero(blind)[0]
+    assert np.all(np.take(gv, idx, axis=-3) == 0), (tag, "masked entries not zero")
+
+
+@pytest.mark.parametrize("i", range(N_CONFIGS))
+def test_random_config(gpu, i):
+    import torch
+    cfg = _draw(i)
+    tag = (i, cfg)
+    d, hq, hkv = cfg["d"], cfg["hq"], cfg["hkv"]
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float16
+    dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(tdt).cuda()
+    kw = dict(causal=cfg["causal"], alpha=cfg["alpha"], window=cfg["window"])
+    if cfg["packed"]:
+        lq, lk = cfg["lens_q"], cfg["lens_k"]
+        cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+        tq, tk = int(cu_q[-1]), int(cu_k[-1])
+        bits, vals = make_qkv_gqa(1, tq, tk, hq, hkv, d, seed=cfg["seed"], dtype=cfg["dtype"])
+        q, k, v = (dev(b[0]) for b in bits)
+        dbits, dvals = make_dout(1, tq, hq, d, seed=cfg["seed"], dtype=cfg["dtype"])
+        do = dev(dbits[0])
+        ex = dict(cu_seqlens_q=torch.from_numpy(cu_q).cuda(), cu_seqlens_k=torch.from_numpy(cu_k).cuda(),
+                  max_seqlen_q=int(max(lq.max(), 1)), max_seqlen_k=int(max(lk.max(), 1)))
+        o, lse = gpu.attention_ex(q, k, v, num_splits=cfg["splits"], **kw, **ex)
+        grads = gpu.attention_backward_ex(q, k, v, o, lse, do, **kw, **ex)
+        torch.cuda.synchronize()
+        o_ref, l_ref = attention_varlen(vals[0][0], vals[1][0], vals[2][0], cu_q, cu_k, cfg["alpha"], cfg["causal"],
+                                        window=cfg["window"])
+        refs = attention_backward_varlen(vals[0][0], vals[1][0], vals[2][0], dvals[0], cu_q, cu_k, cfg["alpha"],
+                                         cfg["causal"], cfg["window"])
+        rows, keys = [], []
+        for a_, b_ in zip(lq, lk):
+            rb, kb = _blind(int(a_), int(b_), cfg["causal"], cfg["window"])
+            rows.append(rb if b_ > 0 else np.ones(int(a_), bool))
+            keys.append(kb if a_ > 0 else np.ones(int(b_), bool))
+        blind = (np.concatenate(rows + [np.zeros(0, bool)]), np.concatenate(keys + [np.zeros(0, bool)]))
+    else:
+        B, nq, nk = cfg["B"], cfg["nq"], cfg["nk"]
+        bits, vals = make_qkv_gqa(B, nq, nk, hq, hkv, d, seed=cfg["seed"], dtype=cfg["dtype"])
+        q, k, v = (dev(b) for b in bits)
+        dbits, dvals = make_dout(B, nq, hq, d, seed=cfg["seed"], dtype=cfg["dtype"])
+        do = dev(dbits)
+        o, lse = gpu.attention_ex(q, k, v, num_splits=cfg["splits"], **kw)
+        grads = gpu.attention_backward_ex(q, k, v, o, lse, do, **kw)
+        torch.cuda.synchronize()
+        o_ref, l_ref = attention_gqa(*vals, cfg["alpha"], cfg["causal"], window=cfg["window"])
+        refs = attention_backward_gqa(*vals, dvals, cfg["alpha"], cfg["causal"], cfg["window"])
+        blind = _blind(nq, nk, cfg["causal"], cfg["window"])
+    og, lg = to_f64(o), to_f64(lse)
+    assert np.all(np.isfinite(og)), tag
+    assert np.array_equal(np.isneginf(lg), np.isneginf(l_ref)), tag
+    err = errors(og, o_ref, lg, l_ref)
+    omax = max(1.0, float(np.abs(o_ref).max()) if o_ref.size else 0.0)
+    assert err["max_abs"] <= 1e-2 * omax, (tag, err, omax)
+    assert err["rmse"] <= 3e-3 and err["lse_abs"] <= 1e-3, (tag, err)
+    for name, g, r_, m in zip(("dq", "dk", "dv"), grads, refs, (blind[0], blind[1], blind[1])):
+        _grad_check(g, r_, m, (tag, name))

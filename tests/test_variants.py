@@ -204,3 +204,22 @@ def test_local_window_decode_and_varlen(gpu, window):
     lens_k, _ = make_seqlens(6, 1, 500, seed=5)
     o, lse, o_ref, l_ref = _varlen(gpu, lens_q, lens_k, 4, 4, 64, False, 2, seed=9, window=window)
     _check(o, lse, o_ref, l_ref, ("varlen", window))
+
+
+def test_no_keys_with_null_key_pointers(gpu):
+    # no sequence has keys: k and v are empty (null data pointers) and every
+    # row gets O = 0, LSE = -inf, dense (N_k = 0) and packed (total_k = 0)
+    import torch
+    q = torch.randn((2, 5, 4, 64), device="cuda").to(torch.bfloat16)
+    k = torch.empty((2, 0, 2, 64), device="cuda", dtype=torch.bfloat16)
+    o, lse = gpu.attention_ex(q, k, k, causal=False, num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    qp = q.reshape(10, 4, 64)
+    kp = torch.empty((0, 2, 64), device="cuda", dtype=torch.bfloat16)
+    cu_q = torch.tensor([0, 4, 10], dtype=torch.int32, device="cuda")
+    cu_k = torch.zeros(3, dtype=torch.int32, device="cuda")
+    o, lse = gpu.attention_ex(qp, kp, kp, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k, max_seqlen_q=6, max_seqlen_k=1,
+                              num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
