@@ -588,6 +588,16 @@ void fwd8_kernel(Fwd8Args a) {
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (DO_SM) finish_tile(Int<SN>{});
+    if constexpr (!DO_QK && !DO_SM) {
+      // The kernel's last PV products: the tails merge here, and the register
+      // copies of the merge read O~ right behind the 16-pass e4m3 MFMA. The
+      // compiler spaces that read 19 wait states from the MFMA, and its last
+      // result registers then come back stale (passes + 4 = 20 is the spacing
+      // it keeps for the 8-pass 16-bit MFMA), so the drain is padded here.
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // prologue: K_0, K_1, V_0 and the descales of tiles 0, 1; S_0, S_1; P_0

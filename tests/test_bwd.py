@@ -74,14 +74,21 @@ def test_bwd_f16_and_alpha(gpu):
 
 
 def test_bwd_delta_is_rowsum_of_dout_times_o(gpu):
+    # the backward is handed the oracle's O (rounded to bf16), so the
+    # expected D = rowsum(dO o O) depends on nothing the GPU computed
     import torch
-    _, _, _, (q, k, v, o, lse, do) = _run(gpu, 1, 77, 3, 64, False, seed=9)
+    from oracle.attention import attention
+    from synth_inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    _, vals, do_vals, (q, k, v, _, lse, do) = _run(gpu, 1, 77, 3, 64, False, seed=9)
     B, N, H, d = q.shape
+    o_ref, _ = attention(*vals, 1 / math.sqrt(d), False)
+    obits = f32_to_bf16_bits(o_ref.astype(np.float32))
+    o_in = torch.from_numpy(obits.view(np.int16)).view(torch.bfloat16).cuda()
     delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    gpu.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, delta)
+    gpu.attn_bwd(q, k, v, o_in, do, lse, dq, dk, dv, delta)
     torch.cuda.synchronize()
-    ref = np.einsum("bnhd,bnhd->bhn", to_f64(do), to_f64(o))
+    ref = np.einsum("bnhd,bnhd->bhn", do_vals, bf16_bits_to_f32(obits).astype(np.float64))
     np.testing.assert_allclose(to_f64(delta), ref, rtol=1e-5, atol=1e-5)
 
 

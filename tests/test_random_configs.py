@@ -139,3 +139,114 @@ def test_random_config(gpu, i):
     assert err["rmse"] <= 3e-3 and err["lse_abs"] <= 1e-3, (tag, err)
     for name, g, r_, m in zip(("dq", "dk", "dv"), grads, refs, (blind[0], blind[1], blind[1])):
         _grad_check(g, r_, m, (tag, name))
+
+
+# ---- decode shapes: few query rows per KV head (the decode kernel) ----------
+
+N_DECODE = 30
+
+
+def _draw_decode(i):
+    r = np.random.default_rng([2025, i])
+    d = int(r.choice([64, 128]))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    g = int(r.choice([1, 2, 4, 8, 16]))
+    nq = int(r.choice([1, 1, 1, 2, 3]))
+    nq = max(1, min(nq, 16 // g))  # N_q * g <= 16 rows per KV head
+    cfg = dict(d=d, hq=hkv * g, hkv=hkv, nq=nq, dtype=str(r.choice(["bf16", "f16"])),
+               causal=bool(r.random() < 0.6), packed=bool(r.random() < 0.3),
+               alpha=None if r.random() < 0.7 else float(r.uniform(0.02, 0.2)),
+               splits=[None, 1, 3, 8][int(r.integers(0, 4))], seed=int(r.integers(0, 10 ** 6)))
+    cfg["window"] = (-1 if r.random() < 0.7 else int(r.integers(1, 500)), -1)
+    if cfg["packed"]:
+        nb = int(r.integers(1, 5))
+        cfg["lens_k"] = r.integers(1, 3000, nb).astype(np.int64)
+        if r.random() < 0.3:
+            cfg["lens_k"][r.integers(0, nb)] = 0
+    else:
+        cfg.update(B=int(r.integers(1, 5)), nk=int(r.integers(1, 3000)))
+    return cfg
+
+
+@pytest.mark.parametrize("i", range(N_DECODE))
+def test_random_decode(gpu, i):
+    import torch
+    cfg = _draw_decode(i)
+    tag = (i, cfg)
+    d, hq, hkv, nq = cfg["d"], cfg["hq"], cfg["hkv"], cfg["nq"]
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float16
+    dev = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(tdt).cuda()
+    kw = dict(causal=cfg["causal"], alpha=cfg["alpha"], window=cfg["window"], num_splits=cfg["splits"])
+    if cfg["packed"]:
+        lk = cfg["lens_k"]
+        lq = np.full(lk.size, nq, dtype=np.int64)
+        cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+        cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+        bits, vals = make_qkv_gqa(1, int(cu_q[-1]), int(cu_k[-1]), hq, hkv, d, seed=cfg["seed"], dtype=cfg["dtype"])
+        q, k, v = (dev(b[0]) for b in bits)
+        o, lse = gpu.attention_ex(q, k, v, cu_seqlens_q=torch.from_numpy(cu_q).cuda(),
+                                  cu_seqlens_k=torch.from_numpy(cu_k).cuda(), max_seqlen_q=nq,
+                                  max_seqlen_k=int(max(lk.max(), 1)), **kw)
+        torch.cuda.synchronize()
+        o_ref, l_ref = attention_varlen(vals[0][0], vals[1][0], vals[2][0], cu_q, cu_k, cfg["alpha"], cfg["causal"],
+                                        window=cfg["window"])
+    else:
+        bits, vals = make_qkv_gqa(cfg["B"], nq, cfg["nk"], hq, hkv, d, seed=cfg["seed"], dtype=cfg["dtype"])
+        q, k, v = (dev(b) for b in bits)
+        o, lse = gpu.attention_ex(q, k, v, **kw)
+        torch.cuda.synchronize()
+        o_ref, l_ref = attention_gqa(*vals, cfg["alpha"], cfg["causal"], window=cfg["window"])
+    og, lg = to_f64(o), to_f64(lse)
+    assert np.all(np.isfinite(og)), tag
+    assert np.array_equal(np.isneginf(lg), np.isneginf(l_ref)), tag
+    err = errors(og, o_ref, lg, l_ref)
+    omax = max(1.0, float(np.abs(o_ref).max()))
+    assert err["max_abs"] <= 1e-2 * omax and err["rmse"] <= 3e-3 and err["lse_abs"] <= 1e-3, (tag, err)
+
+
+# ---- FP8: prepare + forward over random shapes and scale modes --------------
+
+N_FP8 = 20
+
+
+@pytest.mark.parametrize("i", range(N_FP8))
+def test_random_fp8(gpu, i):
+    """<= 1e-2 RMSE against exact attention on the oracle's own dequantised
+    inputs (the kernel's share: P in e4m3, float32 sums). Against the oracle
+    on the unquantised inputs: the FP8 bound, RMSE <= 3e-2, at the standard
+    scale 1/sqrt(d); a larger alpha sharpens the softmax and magnifies the
+    e4m3 error of the scores, which is the inputs' rounding and not the
+    kernel's, so there the bound is the oracle's own quantisation error plus
+    the kernel's share. N stays >= 100: with a handful of keys per row the
+    e4m3 rounding of P (up to 6% per value) dominates whatever the kernel
+    does."""
+    import torch
+    from gpu_util import device_qkv
+    from oracle.attention import attention
+    from oracle.fp8 import emulated_fp8_attention
+    r = np.random.default_rng([2026, i])
+    d = int(r.choice([64, 128, 256]))
+    B, H, N = int(r.integers(1, 3)), int(r.integers(1, 4)), int(r.integers(100, 1200))
+    causal = bool(r.random() < 0.5)
+    block_rows = int(r.choice([0, 128]))
+    had = bool(r.random() < 0.6)
+    alpha = 1 / math.sqrt(d) if r.random() < 0.6 else float(r.uniform(0.02, 0.15))
+    seed = int(r.integers(0, 10 ** 6))
+    outl = {"rate": 1e-3, "factor": 10.0, "kind": "scale"} if r.random() < 0.5 else None
+    tag = (i, d, B, H, N, causal, block_rows, had, alpha, outl is not None)
+    (q, k, v), (qf, kf, vf) = device_qkv(B, N, H, d, seed=seed, outliers=outl)
+    q8, sq = gpu.fp8_prepare(q, block_rows, had, 7)
+    k8, sk = gpu.fp8_prepare(k, block_rows, had, 7)
+    v8, sv = gpu.fp8_prepare(v, block_rows, False, 7)
+    o, lse = gpu.attention_fp8(q8, k8, v8, sq, sk, sv, causal=causal, alpha=alpha, block_rows=block_rows)
+    torch.cuda.synchronize()
+    og = to_f64(o)
+    assert np.isfinite(og).all(), tag
+    o_ref, _ = attention(qf, kf, vf, alpha, causal)
+    o_emu, _ = emulated_fp8_attention(qf, kf, vf, alpha, causal, block_rows, had, 7)
+    rmse = float(math.sqrt(np.mean((og - o_ref) ** 2)))
+    rmse_emu = float(math.sqrt(np.mean((og - o_emu) ** 2)))
+    rmse_quant = float(math.sqrt(np.mean((o_emu - o_ref) ** 2)))
+    assert rmse_emu <= 1e-2, (tag, rmse_emu)
+    bound = 3e-2 if alpha == 1 / math.sqrt(d) else max(3e-2, rmse_quant + 1e-2)
+    assert rmse <= bound, (tag, rmse, rmse_quant)
