@@ -143,6 +143,30 @@ def test_fp8_rmse_and_hadamard_beats_per_tensor_with_outliers(gpu):
         assert res["block+hadamard"] < res["per-tensor"], (N, res)
 
 
+@pytest.mark.parametrize("d,H", [(64, 32), (128, 16), (256, 8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_full_size_sampled(gpu, d, H, causal):
+    """Every head dimension at N = 8192 (B = 2, 16k tokens, hidden 2048), both
+    masks, with the outlier inputs and 128-row blocks + Hadamard: sampled rows
+    (first, last and random, so the causal rows see 1 to 8192 keys) against
+    the oracle on the unquantised inputs."""
+    N, B = 8192, 2
+    (q, k, v), (qf, kf, vf) = device_qkv(B, N, H, d, seed=31 + d, outliers=OUTLIERS)
+    rng = np.random.default_rng(d)
+    samples = [(b, h, np.unique(np.concatenate([[0, 1, 63, 64, N - 1], rng.integers(0, N, 30)])))
+               for b, h in ((0, 0), (B - 1, H - 1))]
+    o, lse = fp8_run(gpu, q, k, v, 128, True, causal)
+    refs = attention_rows(qf, kf, vf, 1 / math.sqrt(d), causal, samples)
+    og = np.concatenate([o[b, rows, h] for b, h, rows in samples])
+    lg = np.concatenate([lse[b, h, rows] for b, h, rows in samples])
+    orf = np.concatenate([r[0] for r in refs])
+    lrf = np.concatenate([r[1] for r in refs])
+    err = errors(og, orf, lg, lrf)
+    print((d, causal), err)
+    assert np.isfinite(o).all()
+    assert err["rmse"] <= 3e-2, err
+
+
 def test_fp8_hadamard_beats_per_tensor_on_full_heads(gpu):
     """The ordering of the outlier benchmark on every row of 8 whole heads
     (N = 2048, B = 8, H = 16, d = 128): a sample of ~130 rows gives a noisy
