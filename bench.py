@@ -331,8 +331,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this attention forward build has no multi-GPU path "
-              "(heads and batch shard across GPUs with no exchange; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (attention heads and "
+              "batch entries are independent, so they would shard across GPUs with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
