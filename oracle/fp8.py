@@ -16,7 +16,7 @@ Sources:
 * "03 · FA3：Hopper 上的异步化与 overlap", section "4. FP8 的两个准确性问题与解法":
   Max_offset = 8 shifts the exponent of P so it uses the e4m3 range.
 
-Readings of points the pages leave open (each also listed in the design notes):
+Readings of points the pages leave open:
 
 * H is the Sylvester-ordered Hadamard matrix (H_1 = [1],
   H_2n = [[H_n, H_n], [H_n, -H_n]]), so d must be a power of two.
