@@ -5,8 +5,9 @@
 // paper review", FP8 section): incoherent processing replaces each row x of Q
 // and K by x M with M = H D / sqrt(d) (H Sylvester-ordered +-1 Hadamard, D a
 // seeded +-1 diagonal), computed as a fast Walsh-Hadamard transform; then
-// every (b, h, 128-row) block (or the whole tensor) gets one float32 scale
-// amax / 448 and its elements are rounded to e4m3. V is quantised without
+// every (b, h, 128-row) block (or the whole tensor) gets one float32 scale,
+// the smallest power of two >= amax / 448, and its elements are rounded to
+// e4m3. V is quantised without
 // the transform. All arithmetic is float32 in a fixed order (butterfly
 // stages h = 1, 2, ..., d/2; one multiply by +-1/sqrt(d); IEEE division by
 // the scale; round-to-nearest-even with saturation at 448) so that the codes
@@ -21,9 +22,10 @@
 // against a reference m that may trail the true max by up to kTau8, so the
 // largest probability is at most 2^(kOff8 + kTau8) < 448, inside e4m3's range
 // (the pages' Max_offset, section 6.5), rounded to e4m3 and fed to the PV product straight from the score
-// registers. O~ is kept in units of the current tile's dv: when the tile's dv
-// differs from the previous one the rescale factor includes dv_prev/dv_cur,
-// and the epilogue multiplies by the last dv and divides by l.
+// registers. Every 128-row block scale is a power of two, and the PV product
+// applies the V tile's scale as the E8M0 scale of its operand, so O~ is in
+// true units and the epilogue only divides by l (with one scale per tensor,
+// O~ is in units of that dv and the epilogue multiplies by it).
 // The V^T operand comes from the row-major V tile through ds_read_b64_tr_b8,
 // the byte-granular transposing LDS read (the pages transpose V inside the
 // kernel through registers; gfx950 does it in the load).
@@ -78,6 +80,16 @@ __device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d
 }
 
 __device__ __forceinline__ float sat448(float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.f), 448.f); }
+
+// Block scale: the smallest power of two >= amax / 448 (IEEE float division),
+// at least 2^-126; 1 when amax is 0. A power of two divides exactly, and its
+// exponent field is the E8M0 scale of the scaled MFMA. The per-tensor scale
+// stays amax / 448: it is one number, which the forward applies at the end.
+__device__ __forceinline__ float block_scale(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  const uint32_t b = __float_as_uint(amax / 448.0f);
+  return __uint_as_float((b & 0x7F800000u) + ((b & 0x007FFFFFu) ? 0x00800000u : 0u));
+}
 
 // MODE 0: per-block scales (block_rows = 128), writes codes and descales.
 // MODE 1: per-tensor amax pass (atomic max of the float bits into descale[0]).
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKernelArgs a) {
     return;
   }
   if (MODE == 2) amax = __uint_as_float(*(const volatile unsigned*)a.descale);
-  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  const float scale = MODE == 0 ? block_scale(amax) : (amax > 0.f ? amax / 448.0f : 1.0f);
   if (MODE == 0 && threadIdx.x == 0) a.descale[(int64_t)bh * a.nblk + blk] = scale;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
@@ -237,6 +249,11 @@ __device__ __forceinline__ f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same product with A scaled by 2^(ea - 127) (E8M0, bias 127) and B by 1.
+__device__ __forceinline__ f32x16 mfma8_scale_a(i32x8 a, i32x8 b, f32x16 c, int ea) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, 127);
+}
+
 struct Fwd8Args {
   const uint8_t* q;
   const uint8_t* k;
@@ -283,11 +300,11 @@ constexpr int kWaves8 = D == 256 ? 1 : 2;
 //
 // Descales. The score scale of tile (i, j) is ct = alpha*log2(e)*dq_i*dk_j and
 // the running max m is kept in those scaled base-2 units; P = 2^(s ct - m +
-// kOff8). O~ is kept in units of the dv of the last tile added: when
-// the next tile's V block has another dv, O~ is multiplied by dv_prev/dv_cur
-// together with the rare rescale ("FlashAttention-3 on Hopper", section 6.3:
-// the descale folded into the O rescale). l sums p in float32 (the pages' row
-// sum), so O = dv_last O~ / l.
+// kOff8). The V block scales are powers of two, and the PV product applies
+// the tile's as the E8M0 scale of its V^T operand, so O~ stays in true units
+// and never needs the dv_prev/dv_cur rescale of the pages' design
+// ("FlashAttention-3 on Hopper", section 6.3: the descale folded into the O
+// rescale). l sums p in float32 (the pages' row sum), so O = O~ / l.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWaves8<D>, kWaves8<D>)))
 void fwd8_kernel(Fwd8Args a) {
@@ -376,8 +393,9 @@ void fwd8_kernel(Fwd8Args a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
   // m_run: the reference (scaled base-2 units); l_run: float32 sum of p;
-  // dv_cur: the dv whose units O~ is in
-  float m_run = -__builtin_inff(), l_run = 0.f, dv_cur = 1.f;
+  // ev: the E8M0 exponent of the V scale of the tile whose P sits in slot X
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  int ev[2] = {127, 127};
 
   const int kv_end = CAUSAL ? min(N, q0 + BM) : N;
   const int nt = (kv_end + BN - 1) / BN;
@@ -506,7 +524,8 @@ void fwd8_kernel(Fwd8Args a) {
     }
   };
   // After the block that added tile j-1 to O~: the rare reference update for
-  // tile j, and O~ moved to tile j's dv units.
+  // tile j, and tile j's V exponent taken while its descale slot still holds
+  // it (the slot is reloaded for tile j+2 before tile j's PV product).
   auto finish_tile = [&](auto sb_tag) ATTN_INLINE {
     constexpr int SB = decltype(sb_tag)::value;
     float f = 1.f;
@@ -523,16 +542,11 @@ void fwd8_kernel(Fwd8Args a) {
       For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<SB>{}, k, Int<1>{}, FalseT{}); });
       l_run *= f;
     }
-    // O~ moves to this tile's dv units only when its V block has another
-    // descale (every other tile with 128-row blocks); the division stays off
-    // the tiles that share the previous block's dv
-    const bool chg = dvt[SB] != dv_cur;
-    if (need || chg) {
-      if (chg) f *= dv_cur / dvt[SB];
+    if (need) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= f;
     }
-    dv_cur = dvt[SB];
+    ev[SB] = nsb ? (int)((__float_as_uint(dvt[SB]) >> 23) & 0xFFu) : 127;
     l_run += r32v;
   };
 
@@ -572,7 +586,7 @@ void fwd8_kernel(Fwd8Args a) {
         constexpr int kc = m / 2, kb = m % 2;
         s[J][kb] = mfma8(op, qreg[kc], kc == 0 ? f32x16{} : s[J][kb]);
       } else {
-        oacc[m - MQK] = mfma8(op, p8[J], oacc[m - MQK]);
+        oacc[m - MQK] = mfma8_scale_a(op, p8[J], oacc[m - MQK], ev[J]);
       }
     };
     if constexpr (DO_SM) tile_scalars(Int<SN>{});
@@ -647,10 +661,10 @@ void fwd8_kernel(Fwd8Args a) {
     iteration(i, Int<0>{}, FalseT{}, FalseT{});
   }
 
-  // finalize: O = O~ dv_cur / l, LSE = (m + log2 l - kOff8) ln 2
+  // finalize: O = O~ / l (per tensor: O~ dv / l), LSE = (m + log2 l - kOff8) ln 2
   const float lt = halves_sum(l_run);
   const bool ok = lt > 0.f;
-  const float inv = ok ? dv_cur / lt : 0.f;
+  const float inv = ok ? (nsb ? 1.f : dvt[0]) / lt : 0.f;
   if (qi < N) {
     if (h32 == 0) {
       const float lse = ok ? (m_run + __builtin_amdgcn_logf(lt) - kOff8) * kLn2 : -__builtin_inff();

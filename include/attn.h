@@ -95,9 +95,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *            (H the Sylvester-ordered +-1 Hadamard matrix, D the diagonal of
  *            signs drawn from `hadamard_seed`), as for Q and K; 0: no
  *            transform (always the case for V). d must be a power of two.
- *   Scale rule: scale = amax / 448 over the block (1 if amax = 0);
- *            code = round-to-nearest-even e4m3 of min(|y / scale|, 448) with
- *            y's sign; descale = scale. All arithmetic is float32.
+ *   Scale rule: per 128-row block, scale = the smallest power of two
+ *            >= amax / 448 (float32 division; at least 2^-126; 1 if
+ *            amax = 0), so that the forward can apply it as an E8M0 MFMA
+ *            scale; per tensor (block_rows = 0), scale = amax / 448 (1 if
+ *            amax = 0). code = round-to-nearest-even e4m3 of
+ *            min(|y / scale|, 448) with y's sign; descale = scale. All
+ *            arithmetic is float32.
  *   Signs:   sign[i] = -1 if bit 63 of splitmix64(hadamard_seed + i) is set,
  *            else +1, where splitmix64(s) is the first output of a SplitMix64
  *            generator with state s.
@@ -117,14 +121,20 @@ int attn_fp8_prepare(const void* x, void* x8, float* descale,
  *            transform). Because (Q M)(K M)^T = Q K^T, the forward needs no
  *            knowledge of M.
  *   descale_q/k/v  float32 descales as written by attn_fp8_prepare with the
- *            same block_rows.
+ *            same block_rows. With block_rows = 128, descale_v must hold
+ *            powers of two (as attn_fp8_prepare writes them): the kernel
+ *            applies only their exponent, as the E8M0 scale of the PV
+ *            product (the "descale folded into the O rescale" of the pages,
+ *            without any rescale).
  *   o        [B, N, H, d] bfloat16 output; lse [B, H, N] float32.
  *   block_rows  128 or 0, matching the descales.
  *   Other arguments as attn_fwd (d = 64, 128 or 256).
  *
  * Scores are accumulated in float32 and multiplied by alpha * dq * dk per
- * tile; P is formed as exp2 of the shifted score plus Max_offset = 8 and
- * rounded to e4m3 for the P V product, whose result is multiplied by dv.
+ * tile; P is formed as exp2 of the score minus a reference that trails the
+ * row maximum by at most 3.8, plus an offset of 5 (the pages' Max_offset,
+ * lowered from 8 so that P <= 2^8.8 < 448 stays inside e4m3), rounded to
+ * e4m3 for the P V product, which applies dv as the V operand's scale.
  */
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse,
                  int B, int H, int N, int d, int causal, float alpha,

@@ -27,8 +27,16 @@ Readings of points the pages leave open:
   splitmix64(x) is the first output of a SplitMix64 generator whose state is x
   (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
   OOPSLA 2014).
-* Scale rule: scale = amax(block) / 448 in float32 (1 if amax = 0);
-  code = e4m3_rne(saturate(x / scale)); descale = scale. Blocks are
+* Scale rule: per 128-row block, scale = the smallest power of two >=
+  amax(block) / 448 (the division in float32; at least 2^-126; 1 if
+  amax = 0); per tensor, scale = amax / 448 (1 if amax = 0). Then code =
+  e4m3_rne(saturate(x / scale)) and descale = scale. The pages fix a
+  per-block scale but not its form. A power of two (an OCP MX E8M0 scale)
+  divides exactly and can be applied by gfx950's scaled MFMA, so the
+  attention kernel never rescales its accumulator when the V block changes;
+  the block's largest value lands in (224, 448] instead of at 448. One
+  scale per tensor never changes, so the per-tensor baseline keeps the
+  plain amax / 448 (its accuracy is the pages' comparison point). Blocks are
   (b, h, 128 consecutive rows of N) over all d; "per tensor" means one scale
   for the whole tensor.
 * The quantiser decides integer codes, so it computes in float32 (the
@@ -157,6 +165,18 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def block_scale(amax):
+    """The smallest power of two >= amax / 448 (float32 division), but at
+    least 2^-126 (the smallest normal float32); 1 when amax is 0."""
+    amax = np.float32(amax)
+    if not amax > 0:
+        return np.float32(1.0)
+    r = np.float32(amax / np.float32(E4M3_MAX))
+    m, e = np.frexp(r)  # r = m * 2^e with 0.5 <= m < 1
+    p = r if m == 0.5 else np.float32(np.ldexp(np.float32(1.0), int(e)))
+    return np.float32(max(p, np.float32(2.0 ** -126)))
+
+
 def quantize(x, block_rows=128, hadamard=False, seed=0):
     """Block (or per-tensor) e4m3 quantisation of a (B, N, H, d) tensor.
 
@@ -186,7 +206,7 @@ def quantize(x, block_rows=128, hadamard=False, seed=0):
             for j in range(nb):
                 blk = y[b, j * block_rows:(j + 1) * block_rows, h, :]
                 amax = np.float32(np.max(np.abs(blk)))
-                scale = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+                scale = block_scale(amax)
                 codes[b, j * block_rows:(j + 1) * block_rows, h, :] = e4m3_encode((blk / scale).astype(np.float32))
                 desc[b, h, j] = scale
     return codes, desc

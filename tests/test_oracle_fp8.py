@@ -119,10 +119,13 @@ def test_e4m3_relative_error_bound_in_normal_range():
 
 @pytest.mark.parametrize("block_rows", [0, 128])
 @pytest.mark.parametrize("hadamard", [False, True])
-def test_quantize_block_max_hits_448_and_dequantizes_closely(block_rows, hadamard):
+def test_quantize_block_max_lands_in_top_binade_and_dequantizes_closely(block_rows, hadamard):
     x, _, _ = make_qkv_f32(2, 300, 3, 64, seed=11, outliers={"rate": 1e-3, "factor": 10})
     codes, desc = quantize(x, block_rows, hadamard, seed=5)
     vals = e4m3_decode(codes)
+    # per tensor, amax / 448: the maximum maps to 448; per block, power-of-two
+    # scales: the block maximum is in (224, 448] before rounding, [224, 448]
+    # after it
     if block_rows == 0:
         assert desc.shape == (1,)
         assert np.abs(vals).max() == E4M3_MAX
@@ -132,7 +135,7 @@ def test_quantize_block_max_hits_448_and_dequantizes_closely(block_rows, hadamar
             for h in range(3):
                 for j in range(3):
                     blk = vals[b, j * 128:(j + 1) * 128, h]
-                    assert np.abs(blk).max() == E4M3_MAX
+                    assert E4M3_MAX / 2 <= np.abs(blk).max() <= E4M3_MAX
     ref = x.astype(np.float64)
     if hadamard:
         ref = ref @ hadamard_matrix(64, 5)
@@ -161,7 +164,19 @@ def test_zero_block_uses_unit_scale():
     x[0, 128:, 0, :] = 3.0
     codes, desc = quantize(x, 128)
     assert desc[0, 0, 0] == 1.0 and np.all(codes[0, :128] == 0)
-    assert desc[0, 0, 1] == np.float32(3.0) / np.float32(448.0)
+    assert desc[0, 0, 1] == np.float32(2.0 ** -7)  # 2^-8 < 3/448 <= 2^-7
+
+
+def test_block_scale_is_the_smallest_power_of_two_covering_amax():
+    from oracle.fp8 import block_scale
+    for amax in (448.0, 449.0, 896.0, 1.0, 3.0, 7.0, 0.001, 1e5, 2.0 ** -100):
+        s = float(block_scale(amax))
+        m, _ = np.frexp(s)
+        assert m == 0.5, (amax, s)                     # a power of two
+        assert s >= amax / 448.0 and s / 2 < amax / 448.0, (amax, s)
+    assert block_scale(448.0) == 1.0 and block_scale(448.5) == 2.0
+    assert block_scale(0.0) == 1.0
+    assert block_scale(1e-40) == np.float32(2.0 ** -126)   # clamped to the smallest normal
 
 
 def test_emulated_fp8_attention_is_close_and_hadamard_helps_with_outliers():
