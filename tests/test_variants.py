@@ -162,6 +162,15 @@ def test_decode_at_serving_size(gpu):
     _check(o, lse, o_ref, l_ref, "decode 8x64/8x8192")
 
 
+@pytest.mark.parametrize("splits", [None, 1])
+def test_decode_long_cache(gpu, splits):
+    # the longest decode the benchmark times: a 32768-key cache, 8 sequences,
+    # 64 query heads over 8 KV heads, d = 128; the heuristic's key ranges and
+    # one range; every row checked
+    o, lse, o_ref, l_ref = _dense(gpu, 8, 1, 32768, 64, 8, 128, True, -1, splits, seed=12)
+    _check(o, lse, o_ref, l_ref, ("decode 8x64/8x32768", splits))
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("nq,g", [(1, 1), (2, 8), (3, 5), (16, 1), (4, 4), (3, 8)])
 def test_few_rows_per_kv_head(gpu, d, nq, g):
