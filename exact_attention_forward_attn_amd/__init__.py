@@ -17,6 +17,8 @@ Functions (same names as the C ABI):
 ``attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False,
 alpha=None, block_rows=128, stream=None)``
     Forward on e4m3 inputs with a bf16 output.
+``attn_fwd_fp8_ex(...)``
+    The same with k8/v8 (and their descales) over fewer key/value heads.
 ``attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None)``
     16-bit backward (d = 64, 128 or 256): gradients dq, dk, dv of the forward's
     O = softmax(alpha q k^T) v for an upstream gradient dout; o and lse are
@@ -47,7 +49,8 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_bwd_ex",
+    "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_fwd_fp8_ex", "attn_bwd",
+    "attn_bwd_ex",
     "attention_backward_ex", "attn_fwd_ex",
     "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
     "attn_last_error", "attention", "attention_ex", "attention_backward", "fp8_prepare", "attention_fp8",
@@ -60,7 +63,8 @@ _lib = None
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 DTYPE_BF16, DTYPE_F16 = 0, 1
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_bwd", "attn_bwd_ex", "attn_fwd_ex",
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_fwd_fp8_ex", "attn_bwd", "attn_bwd_ex",
+                    "attn_fwd_ex",
                     "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
                     "attn_last_error", "attn_version")
 
@@ -94,6 +98,8 @@ def load():
     lib.attn_fp8_prepare.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, i, vp]
     lib.attn_fwd_fp8.restype = i
+    lib.attn_fwd_fp8_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, vp]
+    lib.attn_fwd_fp8_ex.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_bwd.restype = i
     lib.attn_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, i, i,
@@ -298,6 +304,28 @@ def attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=Fal
     return o, lse
 
 
+def attn_fwd_fp8_ex(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False, alpha=None,
+                    block_rows=128, stream=None):
+    """attn_fwd_fp8 with k8/v8 of shape [B, N, Hkv, d], Hq a multiple of Hkv."""
+    torch = _torch()
+    lib = load()
+    B, N, Hq, d = q8.shape
+    Hkv = k8.shape[2] if k8.dim() == 4 else 0
+    _require(q8, "q8", torch.uint8, q8.shape, q8.device)
+    for t, n in ((k8, "k8"), (v8, "v8")):
+        _require(t, n, torch.uint8, (B, N, Hkv, d), q8.device)
+    _require(o, "o", torch.bfloat16, q8.shape, q8.device)
+    _require(lse, "lse", torch.float32, (B, Hq, N), q8.device)
+    nb = (N + block_rows - 1) // block_rows if block_rows else 0
+    _require(descale_q, "descale_q", torch.float32, (B, Hq, nb) if block_rows else (1,), q8.device)
+    for t, n in ((descale_k, "descale_k"), (descale_v, "descale_v")):
+        _require(t, n, torch.float32, (B, Hkv, nb) if block_rows else (1,), q8.device)
+    _check(lib.attn_fwd_fp8_ex(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                               int(bool(causal)), _default_alpha(d, alpha), _ptr(descale_q), _ptr(descale_k),
+                               _ptr(descale_v), int(block_rows), _stream_handle(stream)))
+    return o, lse
+
+
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, delta, causal=False, alpha=None, stream=None):
     """Gradients of O = softmax(alpha q k^T) v: fills dq, dk, dv (and delta)."""
     torch = _torch()
@@ -393,4 +421,5 @@ def attention_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, alp
     B, N, H, d = q8.shape
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
-    return attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, alpha, block_rows, stream)
+    fwd = attn_fwd_fp8 if k8.shape == q8.shape else attn_fwd_fp8_ex
+    return fwd(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, alpha, block_rows, stream)

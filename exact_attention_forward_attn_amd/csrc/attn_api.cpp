@@ -409,26 +409,56 @@ int attn_fp8_prepare(const void* x, void* x8, float* descale, int B, int H, int 
   return hip_status(attn::launch_fp8_prepare(a, stream), "attn_fp8_prepare launch");
 }
 
-int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse, int B, int H, int N,
-                 int d, int causal, float alpha, const float* descale_q, const float* descale_k,
-                 const float* descale_v, int block_rows, void* stream) {
-  const int s = check_fwd_common(q8, k8, v8, o, lse, B, H, N, d, causal, alpha, 1);
+int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, void* o, float* lse, int B, int Hq, int Hkv,
+                    int N, int d, int causal, float alpha, const float* descale_q, const float* descale_k,
+                    const float* descale_v, int block_rows, void* stream) {
+  const int s = check_shape(B, Hq, N, d, 1);
   if (s == 1) return ok();
   if (s != ATTN_OK) return s;
+  if (Hkv < 1 || Hq % Hkv != 0)
+    return fail(ATTN_ERR_INVALID_ARG, "Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
+  if (!std::isfinite(alpha) || alpha < 0.f)
+    return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
   if (block_rows != 0 && block_rows != 128)
     return fail(ATTN_ERR_INVALID_ARG, "block_rows must be 0 or 128 (got %d)", block_rows);
+  const void* ptrs[5] = {q8, k8, v8, o, lse};
+  const char* names[5] = {"q", "k", "v", "o", "lse"};
+  for (int i = 0; i < 5; ++i) {
+    if (!ptrs[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+    if (!aligned16(ptrs[i])) return fail(ATTN_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  }
   const float* ds[3] = {descale_q, descale_k, descale_v};
-  const char* names[3] = {"descale_q", "descale_k", "descale_v"};
+  const char* dnames[3] = {"descale_q", "descale_k", "descale_v"};
   for (int i = 0; i < 3; ++i)
-    if (!ds[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", names[i]);
+    if (!ds[i]) return fail(ATTN_ERR_INVALID_ARG, "%s is null", dnames[i]);
+  const int64_t q_bytes = (int64_t)B * N * Hq * d;
+  const int64_t kv_bytes = (int64_t)B * N * Hkv * d;
+  const int64_t out_bytes = (int64_t)B * N * Hq * d * 2;
+  const int64_t lse_bytes = (int64_t)B * Hq * N * 4;
+  const void* ins[3] = {q8, k8, v8};
+  const int64_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, out_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_INVALID_ARG, "o overlaps %s", names[i]);
+    if (overlaps(lse, lse_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_INVALID_ARG, "lse overlaps %s", names[i]);
+  }
+  if (overlaps(o, out_bytes, lse, lse_bytes)) return fail(ATTN_ERR_INVALID_ARG, "o overlaps lse");
   attn::FwdArgs a{};
   a.q = q8; a.k = k8; a.v = v8; a.o = o; a.lse = lse;
   a.dq = descale_q; a.dk = descale_k; a.dv = descale_v;
-  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.B = B; a.H = Hq; a.N = N; a.d = d;
+  a.Hkv = Hkv;
   a.causal = causal;
   a.block_rows = block_rows;
   a.scale_log2 = scale_log2(alpha);
   return hip_status(attn::launch_fwd_fp8(a, stream), "attn_fwd_fp8 launch");
+}
+
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse, int B, int H, int N,
+                 int d, int causal, float alpha, const float* descale_q, const float* descale_k,
+                 const float* descale_v, int block_rows, void* stream) {
+  return attn_fwd_fp8_ex(q8, k8, v8, o, lse, B, H, H, N, d, causal, alpha, descale_q, descale_k, descale_v,
+                         block_rows, stream);
 }
 
 const char* attn_last_error(void) { return g_err.c_str(); }

@@ -264,8 +264,9 @@ struct Fwd8Args {
   const float* dk;
   const float* dv;
   int B, H, N;
+  int Hkv;        // key/value heads; query head h reads head h / (H / Hkv)
   int n_mblk;
-  int nsb;        // descale blocks per (b, h): ceil(N/128), or 0 for per-tensor
+  int nsb;        // descale blocks per (b, head): ceil(N/128), or 0 for per-tensor
   float c;        // alpha * log2(e)
 };
 
@@ -337,17 +338,24 @@ void fwd8_kernel(Fwd8Args a) {
   const uint32_t RS = (uint32_t)a.H * D;
   const int64_t head_off = ((int64_t)b * N * a.H + hh) * D;
   const uint32_t span = (uint32_t)(N - 1) * RS + D;
+  // grouped heads ("FlashAttention-3 on Hopper", section 5.6.1): the
+  // key/value head of query head hh, and its row stride
+  const int hk = hh / (a.H / a.Hkv);
+  const uint32_t RSK = (uint32_t)a.Hkv * D;
+  const int64_t kv_off = ((int64_t)b * N * a.Hkv + hk) * D;
+  const uint32_t span_kv = (uint32_t)(N - 1) * RSK + D;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + head_off, span);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + head_off, span);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + head_off, span);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + kv_off, span_kv);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + kv_off, span_kv);
 
   // descales of this head: one per 128-row block, or one per tensor
   const int nsb = a.nsb;
   const int64_t sb0 = nsb ? (int64_t)bh * nsb : 0;
+  const int64_t sbk0 = nsb ? ((int64_t)b * a.Hkv + hk) * nsb : 0;
   const uint32_t nsb_bytes = (uint32_t)(nsb ? nsb : 1) * 4;
-  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + sb0, nsb_bytes);
-  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + sb0, nsb_bytes);
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(a.dk + sbk0, nsb_bytes);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(a.dv + sbk0, nsb_bytes);
   auto sblk = [&](int row) ATTN_INLINE { return nsb ? row / 128 : 0; };
 
   // Q^T operands: dims 64kc + 32*h32 .. +31 of query row qi
@@ -368,8 +376,8 @@ void fwd8_kernel(Fwd8Args a) {
     const int seg = wave + 4 * t;
     const int r = seg * G::RPS + lane / G::CPR;
     const int pc = lane % G::CPR;
-    kg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_rows<G::ROWB>(r)) << 4);
-    vg[t] = (uint32_t)r * RS + (uint32_t)((pc ^ swz_v8<G::ROWB>(r)) << 4);
+    kg[t] = (uint32_t)r * RSK + (uint32_t)((pc ^ swz_rows<G::ROWB>(r)) << 4);
+    vg[t] = (uint32_t)r * RSK + (uint32_t)((pc ^ swz_v8<G::ROWB>(r)) << 4);
   }
   // K operand: row kb*32 + l32, chunks 4kc + 2*h32 + u
   int kofs[KC][2];
@@ -410,7 +418,7 @@ void fwd8_kernel(Fwd8Args a) {
   auto kslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? kbuf1 : kbuf0; };
   auto vslot = [&](auto j) ATTN_INLINE -> char* { return (decltype(j)::value & 1) ? vbuf1 : vbuf0; };
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) ATTN_INLINE {
-    const uint32_t base = (uint32_t)((nt - 1 - i) * BN) * RS;
+    const uint32_t base = (uint32_t)((nt - 1 - i) * BN) * RSK;
 #pragma unroll
     for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
       const uint32_t voff = (is_k ? kg[t] : vg[t]) + base;
@@ -693,6 +701,7 @@ int launch_fwd(const FwdArgs& f, hipStream_t st) {
   a.o = (__bf16*)f.o; a.lse = f.lse;
   a.dq = f.dq; a.dk = f.dk; a.dv = f.dv;
   a.B = f.B; a.H = f.H; a.N = f.N;
+  a.Hkv = f.Hkv > 0 ? f.Hkv : f.H;
   a.n_mblk = (f.N + BM - 1) / BM;
   a.nsb = f.block_rows ? (f.N + f.block_rows - 1) / f.block_rows : 0;
   a.c = f.scale_log2;

@@ -142,6 +142,24 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
                  int block_rows, void* stream);
 
 /*
+ * attn_fwd_fp8_ex -- attn_fwd_fp8 with grouped key/value heads ("FlashAttention-3
+ * on Hopper", section 5.6.1: GQA/MQA).
+ *
+ *   q8       [B, N, Hq, d] e4m3; o [B, N, Hq, d] bfloat16; lse [B, Hq, N].
+ *   k8, v8   [B, N, Hkv, d] e4m3; query head h reads key/value head
+ *            h / (Hq / Hkv). Hq must be a positive multiple of Hkv (Hkv = 1 is
+ *            multi-query attention).
+ *   descale_q  as written by attn_fp8_prepare for q8 (H = Hq);
+ *   descale_k/v as written by attn_fp8_prepare for k8 and v8 (H = Hkv).
+ *   Other arguments, layouts and errors as attn_fwd_fp8, which is this call
+ *   with Hkv = Hq.
+ */
+int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, void* o, float* lse,
+                    int B, int Hq, int Hkv, int N, int d, int causal, float alpha,
+                    const float* descale_q, const float* descale_k, const float* descale_v,
+                    int block_rows, void* stream);
+
+/*
  * attn_bwd -- gradients of the exact attention forward ("FlashAttention-3 on
  * Hopper", chapter 7, section 7.1): for O = softmax(alpha Q K^T) V and an
  * upstream gradient dO,

@@ -124,6 +124,35 @@ def test_fp8_forward_rejects_bad_arguments(kw, status, msg):
     assert msg in ea.attn_last_error()
 
 
+def _fwd8_ex(**kw):
+    lib = ea.load()
+    a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000, lse=FAKE + 0x40000000,
+             B=1, Hq=4, Hkv=2, N=256, d=128, causal=0, alpha=0.1, dq=FAKE + 0x50000000, dk=FAKE + 0x50001000,
+             dv=FAKE + 0x50002000, block_rows=128, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_fp8_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                               a["d"], a["causal"], a["alpha"], a["dq"], a["dk"], a["dv"], a["block_rows"],
+                               a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(Hkv=0), ea.ATTN_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(block_rows=64), ea.ATTN_ERR_INVALID_ARG, "block_rows"),
+    (dict(dv=None), ea.ATTN_ERR_INVALID_ARG, "descale_v is null"),
+    (dict(k=None), ea.ATTN_ERR_INVALID_ARG, "k is null"),
+    (dict(o=FAKE + 0x10000000 + 0x100), ea.ATTN_ERR_INVALID_ARG, "o overlaps k"),
+])
+def test_fp8_forward_ex_rejects_bad_arguments(kw, status, msg):
+    assert _fwd8_ex(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def test_fp8_forward_ex_empty_problems_are_no_ops():
+    assert _fwd8_ex(N=0) == ea.ATTN_OK
+    assert _fwd8_ex(B=0, Hkv=0) == ea.ATTN_OK
+
+
 def _bwd(**kw):
     lib = ea.load()
     names = ("q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "delta")

@@ -119,6 +119,37 @@ def test_fp8_every_tail_tracks_emulated_reference(gpu, d, causal, N):
     assert err["lse_abs"] <= 5e-3, err
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 1), (6, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block_rows", [128, 0])
+def test_fp8_grouped_heads(gpu, hq, hkv, causal, block_rows):
+    """attn_fwd_fp8_ex: query head h reads key/value head h / (Hq / Hkv).
+    Against exact grouped attention on the oracle's own dequantised inputs
+    (the kernel's share) and on the unquantised inputs (the FP8 bound)."""
+    import torch
+    from oracle.fp8 import dequantize
+    from oracle.variants import attention_gqa
+    from synth_inputs import make_qkv_gqa
+    B, N, d = 2, 300, 128
+    bits, (qf, kf, vf) = make_qkv_gqa(B, N, N, hq, hkv, d, seed=hq * 10 + hkv)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda() for b in bits)
+    q8, sq = gpu.fp8_prepare(q, block_rows, True, 7)
+    k8, sk = gpu.fp8_prepare(k, block_rows, True, 7)
+    v8, sv = gpu.fp8_prepare(v, block_rows, False, 7)
+    o, lse = gpu.attention_fp8(q8, k8, v8, sq, sk, sv, causal=causal, block_rows=block_rows)
+    torch.cuda.synchronize()
+    o, lse = to_f64(o), lse.cpu().numpy().astype(np.float64)
+    deq = [dequantize(*quantize(x, block_rows, had, 7), block_rows)
+           for x, had in ((qf, True), (kf, True), (vf, False))]
+    o_emu, l_emu = attention_gqa(deq[0], deq[1], deq[2], 1 / math.sqrt(d), causal)
+    o_ref, l_ref = attention_gqa(qf, kf, vf, 1 / math.sqrt(d), causal)
+    err_emu = errors(o, o_emu, lse, l_emu)
+    err = errors(o, o_ref, lse, l_ref)
+    print((hq, hkv, causal, block_rows), err_emu, err)
+    assert err_emu["rmse"] <= 1e-2 and err_emu["lse_abs"] <= 5e-3, err_emu
+    assert err["rmse"] <= 3e-2, err
+
+
 def test_fp8_rmse_and_hadamard_beats_per_tensor_with_outliers(gpu):
     """The FP8 configuration of the benchmark: H=16, d=128, N in 1k..16k,
     B = 16k/N, N(0,1) inputs with 0.1% of entries scaled by 10. Compared on
