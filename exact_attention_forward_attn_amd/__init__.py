@@ -15,7 +15,7 @@ Functions (same names as the C ABI):
     Hadamard transform (optional) + block quantisation of a bf16 tensor to
     e4m3 codes (uint8) and float32 descales.
 ``attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False,
-alpha=None, block_rows=128, stream=None)``
+alpha=None, block_rows=128, hadamard_seed=0, stream=None)``
     Forward on e4m3 inputs with a bf16 output.
 ``attn_fwd_fp8_ex(...)``
     The same with k8/v8 (and their descales) over fewer key/value heads.
@@ -96,9 +96,10 @@ def load():
     lib.attn_fwd.restype = i
     lib.attn_fp8_prepare.argtypes = [vp, vp, vp, i, i, i, i, i, i, ctypes.c_uint64, vp]
     lib.attn_fp8_prepare.restype = i
-    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, i, vp]
+    u64 = ctypes.c_uint64
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, i, u64, vp]
     lib.attn_fwd_fp8.restype = i
-    lib.attn_fwd_fp8_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, vp]
+    lib.attn_fwd_fp8_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, vp, vp, i, u64, vp]
     lib.attn_fwd_fp8_ex.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.attn_bwd.restype = i
@@ -285,9 +286,15 @@ def attn_fp8_prepare(x, x8, descale, block_rows=128, hadamard=False, seed=0, str
     return x8, descale
 
 
+def _seed(seed):
+    return ctypes.c_uint64(int(seed) & (2 ** 64 - 1))
+
+
 def attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False, alpha=None,
-                 block_rows=128, stream=None):
-    """Forward on e4m3 codes from attn_fp8_prepare; o is bf16."""
+                 block_rows=128, hadamard_seed=0, stream=None):
+    """Forward on e4m3 codes from attn_fp8_prepare; o is bf16. hadamard_seed
+    is the seed q8 and k8 were prepared with (a contract the library cannot
+    check: the forward never applies the transform)."""
     torch = _torch()
     lib = load()
     B, N, H, d = q8.shape
@@ -300,12 +307,12 @@ def attn_fwd_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=Fal
         _require(t, n, torch.float32, nd, q8.device)
     _check(lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, H, N, d,
                             int(bool(causal)), _default_alpha(d, alpha), _ptr(descale_q), _ptr(descale_k),
-                            _ptr(descale_v), int(block_rows), _stream_handle(stream)))
+                            _ptr(descale_v), int(block_rows), _seed(hadamard_seed), _stream_handle(stream)))
     return o, lse
 
 
 def attn_fwd_fp8_ex(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=False, alpha=None,
-                    block_rows=128, stream=None):
+                    block_rows=128, hadamard_seed=0, stream=None):
     """attn_fwd_fp8 with k8/v8 of shape [B, N, Hkv, d], Hq a multiple of Hkv."""
     torch = _torch()
     lib = load()
@@ -322,7 +329,7 @@ def attn_fwd_fp8_ex(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal=
         _require(t, n, torch.float32, (B, Hkv, nb) if block_rows else (1,), q8.device)
     _check(lib.attn_fwd_fp8_ex(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
                                int(bool(causal)), _default_alpha(d, alpha), _ptr(descale_q), _ptr(descale_k),
-                               _ptr(descale_v), int(block_rows), _stream_handle(stream)))
+                               _ptr(descale_v), int(block_rows), _seed(hadamard_seed), _stream_handle(stream)))
     return o, lse
 
 
@@ -416,10 +423,11 @@ def fp8_prepare(x, block_rows=128, hadamard=False, seed=0, stream=None):
 
 
 def attention_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, alpha=None, block_rows=128,
-                  stream=None):
+                  hadamard_seed=0, stream=None):
     torch = _torch()
     B, N, H, d = q8.shape
     o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     fwd = attn_fwd_fp8 if k8.shape == q8.shape else attn_fwd_fp8_ex
-    return fwd(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, alpha, block_rows, stream)
+    return fwd(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, alpha, block_rows, hadamard_seed,
+               stream)

@@ -161,10 +161,16 @@ int attn_num_splits_heuristic(int B, int Hq, int Hkv, int Nq, int Nk, int d, int
   return s < 1 ? 1 : (int)s;
 }
 
-int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+}  // extern "C"
+
+namespace {
+
+// The body of attn_fwd_ex (what names the entry point in error messages).
+int fwd_ex_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                 int Nq, int Nk, int d, const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q,
                 int total_k, int causal, int window_left, int window_right, float alpha, int dtype,
-                int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes, void* stream) {
+                int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes, const char* what,
+                void* stream) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
@@ -268,7 +274,20 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     a.opart = workspace;
     a.lpart = workspace + (int64_t)nsplit * total_q * Hq * d;
   }
-  return hip_status(attn::launch_fwd_16(a, stream), "attn_fwd_ex launch");
+  return hip_status(attn::launch_fwd_16(a, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                int Nq, int Nk, int d, const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q,
+                int total_k, int causal, int window_left, int window_right, float alpha, int dtype,
+                int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes, void* stream) {
+  return fwd_ex_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k, causal,
+                     window_left, window_right, alpha, dtype, pack_gqa, num_splits, workspace, workspace_bytes,
+                     "attn_fwd_ex", stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -411,12 +430,18 @@ int attn_fp8_prepare(const void* x, void* x8, float* descale, int B, int H, int 
 
 int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, void* o, float* lse, int B, int Hq, int Hkv,
                     int N, int d, int causal, float alpha, const float* descale_q, const float* descale_k,
-                    const float* descale_v, int block_rows, void* stream) {
+                    const float* descale_v, int block_rows, uint64_t hadamard_seed, void* stream) {
+  // The seed only names the transform q8 and k8 were prepared with: the
+  // product (Q M)(K M)^T equals Q K^T for the orthogonal M, so the forward
+  // never applies M, and nothing in the codes records which M was used.
+  (void)hadamard_seed;
+  // the head grouping is checked before the empty-problem return, as in
+  // attn_fwd_ex
+  if (Hq > 0 && (Hkv < 1 || Hq % Hkv != 0))
+    return fail(ATTN_ERR_INVALID_ARG, "Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
   const int s = check_shape(B, Hq, N, d, 1);
   if (s == 1) return ok();
   if (s != ATTN_OK) return s;
-  if (Hkv < 1 || Hq % Hkv != 0)
-    return fail(ATTN_ERR_INVALID_ARG, "Hq = %d must be a positive multiple of Hkv = %d", Hq, Hkv);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_INVALID_ARG, "causal must be 0 or 1 (got %d)", causal);
   if (!std::isfinite(alpha) || alpha < 0.f)
     return fail(ATTN_ERR_INVALID_ARG, "alpha must be finite and >= 0 (got %g)", (double)alpha);
@@ -443,6 +468,15 @@ int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, void* o, flo
     if (overlaps(lse, lse_bytes, ins[i], in_bytes[i])) return fail(ATTN_ERR_INVALID_ARG, "lse overlaps %s", names[i]);
   }
   if (overlaps(o, out_bytes, lse, lse_bytes)) return fail(ATTN_ERR_INVALID_ARG, "o overlaps lse");
+  // the kernel writes o and lse while it reads the descales
+  const int64_t nsb = block_rows ? ((int64_t)N + block_rows - 1) / block_rows : 0;
+  const int64_t ds_bytes[3] = {block_rows ? (int64_t)B * Hq * nsb * 4 : 4, block_rows ? (int64_t)B * Hkv * nsb * 4 : 4,
+                               block_rows ? (int64_t)B * Hkv * nsb * 4 : 4};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(o, out_bytes, ds[i], ds_bytes[i])) return fail(ATTN_ERR_INVALID_ARG, "o overlaps %s", dnames[i]);
+    if (overlaps(lse, lse_bytes, ds[i], ds_bytes[i]))
+      return fail(ATTN_ERR_INVALID_ARG, "lse overlaps %s", dnames[i]);
+  }
   attn::FwdArgs a{};
   a.q = q8; a.k = k8; a.v = v8; a.o = o; a.lse = lse;
   a.dq = descale_q; a.dk = descale_k; a.dv = descale_v;
@@ -456,9 +490,9 @@ int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, void* o, flo
 
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse, int B, int H, int N,
                  int d, int causal, float alpha, const float* descale_q, const float* descale_k,
-                 const float* descale_v, int block_rows, void* stream) {
+                 const float* descale_v, int block_rows, uint64_t hadamard_seed, void* stream) {
   return attn_fwd_fp8_ex(q8, k8, v8, o, lse, B, H, H, N, d, causal, alpha, descale_q, descale_k, descale_v,
-                         block_rows, stream);
+                         block_rows, hadamard_seed, stream);
 }
 
 const char* attn_last_error(void) { return g_err.c_str(); }

@@ -128,7 +128,15 @@ int attn_fp8_prepare(const void* x, void* x8, float* descale,
  *            without any rescale).
  *   o        [B, N, H, d] bfloat16 output; lse [B, H, N] float32.
  *   block_rows  128 or 0, matching the descales.
- *   Other arguments as attn_fwd (d = 64, 128 or 256).
+ *   hadamard_seed  the seed q8 and k8 were prepared with (attn_fp8_prepare,
+ *            hadamard = 1); any value when they were prepared without the
+ *            transform. It is a contract, not an input to the arithmetic:
+ *            Q and K must share one M for (Q M)(K M)^T = Q K^T to hold
+ *            ("FlashAttention-3 on Hopper", section 6.4), the forward never
+ *            applies M, and the codes do not record which M was used, so a
+ *            mismatch cannot be detected and gives wrong scores.
+ *   Other arguments as attn_fwd (d = 64, 128 or 256). The descales must not
+ *   overlap o or lse.
  *
  * Scores are accumulated in float32 and multiplied by alpha * dq * dk per
  * tile; P is formed as exp2 of the score minus a reference that trails the
@@ -139,7 +147,7 @@ int attn_fp8_prepare(const void* x, void* x8, float* descale,
 int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float* lse,
                  int B, int H, int N, int d, int causal, float alpha,
                  const float* descale_q, const float* descale_k, const float* descale_v,
-                 int block_rows, void* stream);
+                 int block_rows, uint64_t hadamard_seed, void* stream);
 
 /*
  * attn_fwd_fp8_ex -- attn_fwd_fp8 with grouped key/value heads ("FlashAttention-3
@@ -151,13 +159,14 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
  *            multi-query attention).
  *   descale_q  as written by attn_fp8_prepare for q8 (H = Hq);
  *   descale_k/v as written by attn_fp8_prepare for k8 and v8 (H = Hkv).
+ *   Hkv is checked before an empty problem returns (as in attn_fwd_ex).
  *   Other arguments, layouts and errors as attn_fwd_fp8, which is this call
  *   with Hkv = Hq.
  */
 int attn_fwd_fp8_ex(const void* q8, const void* k8, const void* v8, void* o, float* lse,
                     int B, int Hq, int Hkv, int N, int d, int causal, float alpha,
                     const float* descale_q, const float* descale_k, const float* descale_v,
-                    int block_rows, void* stream);
+                    int block_rows, uint64_t hadamard_seed, void* stream);
 
 /*
  * attn_bwd -- gradients of the exact attention forward ("FlashAttention-3 on
@@ -255,6 +264,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
 /* Workspace bytes attn_fwd_ex needs for num_splits key ranges (0 for
  * num_splits <= 1): num_splits * total_q * Hq * (d + 1) * 4. */
 int64_t attn_splitkv_workspace_bytes(int num_splits, int total_q, int Hq, int d);
+
 
 /* 1 if packing the query heads of a group takes fewer 128-row query tiles
  * than one head per tile (e.g. decode with Nq = 1 and Hq > Hkv), else 0. */

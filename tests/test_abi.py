@@ -107,10 +107,11 @@ def _fwd8(**kw):
     lib = ea.load()
     a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000, lse=FAKE + 0x40000000,
              B=1, H=2, N=256, d=128, causal=0, alpha=0.1, dq=FAKE + 0x50000000, dk=FAKE + 0x50001000,
-             dv=FAKE + 0x50002000, block_rows=128, stream=None)
+             dv=FAKE + 0x50002000, block_rows=128, seed=0, stream=None)
     a.update(kw)
     return lib.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
-                            a["causal"], a["alpha"], a["dq"], a["dk"], a["dv"], a["block_rows"], a["stream"])
+                            a["causal"], a["alpha"], a["dq"], a["dk"], a["dv"], a["block_rows"],
+                            ctypes.c_uint64(a["seed"]), a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -124,15 +125,32 @@ def test_fp8_forward_rejects_bad_arguments(kw, status, msg):
     assert msg in ea.attn_last_error()
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2 ** 63 + 5, 2 ** 64 - 1])
+def test_fp8_forward_takes_any_hadamard_seed(seed):
+    # the seed is a contract on how q8 and k8 were prepared, never validated:
+    # every 64-bit value passes the argument checks (a bad block_rows still
+    # fails afterwards, so nothing is launched)
+    assert _fwd8(seed=seed, block_rows=32) == ea.ATTN_ERR_INVALID_ARG
+    assert "block_rows" in ea.attn_last_error()
+    assert _fwd8_ex(seed=seed, block_rows=32) == ea.ATTN_ERR_INVALID_ARG
+    assert _fwd8(seed=seed, N=0) == ea.ATTN_OK
+
+
+def test_fp8_forward_binding_passes_the_seed_as_uint64():
+    lib = ea.load()
+    for fn in (lib.attn_fwd_fp8, lib.attn_fwd_fp8_ex):
+        assert fn.argtypes[-2] is ctypes.c_uint64 and fn.argtypes[-1] is ctypes.c_void_p
+
+
 def _fwd8_ex(**kw):
     lib = ea.load()
     a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000, lse=FAKE + 0x40000000,
              B=1, Hq=4, Hkv=2, N=256, d=128, causal=0, alpha=0.1, dq=FAKE + 0x50000000, dk=FAKE + 0x50001000,
-             dv=FAKE + 0x50002000, block_rows=128, stream=None)
+             dv=FAKE + 0x50002000, block_rows=128, seed=0, stream=None)
     a.update(kw)
     return lib.attn_fwd_fp8_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
                                a["d"], a["causal"], a["alpha"], a["dq"], a["dk"], a["dv"], a["block_rows"],
-                               a["stream"])
+                               ctypes.c_uint64(a["seed"]), a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -142,6 +160,11 @@ def _fwd8_ex(**kw):
     (dict(dv=None), ea.ATTN_ERR_INVALID_ARG, "descale_v is null"),
     (dict(k=None), ea.ATTN_ERR_INVALID_ARG, "k is null"),
     (dict(o=FAKE + 0x10000000 + 0x100), ea.ATTN_ERR_INVALID_ARG, "o overlaps k"),
+    # the kernel writes o and lse while it reads the descales
+    (dict(dq=FAKE + 0x30000000 + 0x40), ea.ATTN_ERR_INVALID_ARG, "o overlaps descale_q"),
+    (dict(dk=FAKE + 0x40000000 + 0x10), ea.ATTN_ERR_INVALID_ARG, "lse overlaps descale_k"),
+    (dict(dv=FAKE + 0x40000000 + 0x800), ea.ATTN_ERR_INVALID_ARG, "lse overlaps descale_v"),
+    (dict(dv=FAKE + 0x30000000, block_rows=0), ea.ATTN_ERR_INVALID_ARG, "o overlaps descale_v"),
 ])
 def test_fp8_forward_ex_rejects_bad_arguments(kw, status, msg):
     assert _fwd8_ex(**kw) == status
@@ -150,7 +173,16 @@ def test_fp8_forward_ex_rejects_bad_arguments(kw, status, msg):
 
 def test_fp8_forward_ex_empty_problems_are_no_ops():
     assert _fwd8_ex(N=0) == ea.ATTN_OK
-    assert _fwd8_ex(B=0, Hkv=0) == ea.ATTN_OK
+    assert _fwd8_ex(B=0) == ea.ATTN_OK
+    assert _fwd8_ex(Hq=0, Hkv=0) == ea.ATTN_OK
+
+
+@pytest.mark.parametrize("kw", [dict(N=0, Hkv=3), dict(B=0, Hkv=0), dict(N=0, Hq=4, Hkv=8)])
+def test_fp8_forward_ex_checks_head_grouping_before_the_empty_return(kw):
+    # the same grouping attn_fwd_ex rejects is rejected here even when the
+    # problem is empty
+    assert _fwd8_ex(**kw) == ea.ATTN_ERR_INVALID_ARG
+    assert "multiple of Hkv" in ea.attn_last_error()
 
 
 def _bwd(**kw):
