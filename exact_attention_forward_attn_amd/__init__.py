@@ -30,6 +30,9 @@ max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, workspace=None,
     packed variable-length batches (int32 cu_seqlens) and split-KV. Dense:
     q, o [B, Nq, Hq, d], k, v [B, Nk, Hkv, d], lse [B, Hq, Nq]. Packed:
     q, o [total_q, Hq, d], k, v [total_k, Hkv, d], lse [Hq, total_q].
+``attn_fwd_ex_noalloc(q, k, v, o, lse, ...)``
+    attn_fwd_ex without the workspace argument (for callers that cannot
+    allocate): split-KV states go to a static 16 MiB array per GPU.
 ``attn_splitkv_workspace_bytes``, ``attn_pack_gqa_heuristic``,
 ``attn_num_splits_heuristic``
     Sizing helpers of attn_fwd_ex (pure host functions).
@@ -51,7 +54,7 @@ import os
 __all__ = [
     "AttnError", "load", "lib_path", "attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_fwd_fp8_ex", "attn_bwd",
     "attn_bwd_ex",
-    "attention_backward_ex", "attn_fwd_ex",
+    "attention_backward_ex", "attn_fwd_ex", "attn_fwd_ex_noalloc", "STATIC_WORKSPACE_BYTES",
     "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
     "attn_last_error", "attention", "attention_ex", "attention_backward", "fp8_prepare", "attention_fp8",
     "EXPORTED_SYMBOLS",
@@ -64,7 +67,7 @@ _lib = None
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, -1, -2, -3
 DTYPE_BF16, DTYPE_F16 = 0, 1
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fp8_prepare", "attn_fwd_fp8", "attn_fwd_fp8_ex", "attn_bwd", "attn_bwd_ex",
-                    "attn_fwd_ex",
+                    "attn_fwd_ex", "attn_fwd_ex_noalloc",
                     "attn_splitkv_workspace_bytes", "attn_pack_gqa_heuristic", "attn_num_splits_heuristic",
                     "attn_last_error", "attn_version")
 
@@ -109,6 +112,8 @@ def load():
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, i, i, f, i, i, i, vp,
                                 ctypes.c_int64, vp]
     lib.attn_fwd_ex.restype = i
+    lib.attn_fwd_ex_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.attn_fwd_ex_noalloc.restype = i
     lib.attn_splitkv_workspace_bytes.argtypes = [i, i, i, i]
     lib.attn_splitkv_workspace_bytes.restype = ctypes.c_int64
     lib.attn_pack_gqa_heuristic.argtypes = [i, i, i]
@@ -248,6 +253,42 @@ def attn_fwd_ex(q, k, v, o, lse, causal=False, alpha=None, cu_seqlens_q=None, cu
                            total_q, total_k, int(bool(causal)), int(window[0]), int(window[1]),
                            _default_alpha(d, alpha), dt, int(pack_gqa),
                            int(num_splits), ws, ctypes.c_int64(ws_bytes), _stream_handle(stream)))
+    return o, lse
+
+
+STATIC_WORKSPACE_BYTES = 16 << 20  # ATTN_STATIC_WORKSPACE_BYTES of include/attn.h
+
+
+def attn_fwd_ex_noalloc(q, k, v, o, lse, causal=False, alpha=None, cu_seqlens_q=None, cu_seqlens_k=None,
+                        max_seqlen_q=None, max_seqlen_k=None, pack_gqa=-1, num_splits=1, stream=None,
+                        window=(-1, -1)):
+    """attn_fwd_ex without a workspace argument: the split-KV range states go
+    to the library's static per-GPU array (STATIC_WORKSPACE_BYTES), so the
+    call allocates no device memory. Calls that overlap in time on one GPU
+    race on that array."""
+    torch = _torch()
+    lib = load()
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    if (cu_seqlens_q is None) != (cu_seqlens_k is None):
+        raise ValueError("give both cu_seqlens_q and cu_seqlens_k, or neither")
+    B, Hq, Hkv, Nq, Nk, d, total_q, total_k, lse_shape = _ex_shapes(q, k, cu_seqlens_q, cu_seqlens_k,
+                                                                    max_seqlen_q, max_seqlen_k)
+    _require(q, "q", q.dtype, q.shape, q.device)
+    _require(o, "o", q.dtype, q.shape, q.device)
+    _require(k, "k", q.dtype, k.shape, q.device)
+    _require(v, "v", q.dtype, k.shape, q.device)
+    _require(lse, "lse", torch.float32, lse_shape, q.device)
+    cu_q = cu_k = ctypes.c_void_p(0)
+    if cu_seqlens_q is not None:
+        _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, (B + 1,), q.device)
+        _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, (B + 1,), q.device)
+        cu_q, cu_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_F16
+    _check(lib.attn_fwd_ex_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, cu_q, cu_k,
+                                   total_q, total_k, int(bool(causal)), int(window[0]), int(window[1]),
+                                   _default_alpha(d, alpha), dt, int(pack_gqa), int(num_splits),
+                                   _stream_handle(stream)))
     return o, lse
 
 

@@ -16,6 +16,8 @@
 
 #include "attn_internal.h"
 
+static_assert(attn::kStaticWorkspaceBytes == ATTN_STATIC_WORKSPACE_BYTES, "header and library disagree");
+
 namespace {
 
 thread_local std::string g_err;
@@ -165,12 +167,14 @@ int attn_num_splits_heuristic(int B, int Hq, int Hkv, int Nq, int Nk, int d, int
 
 namespace {
 
-// The body of attn_fwd_ex (what names the entry point in error messages).
+// attn_fwd_ex, with the split-KV workspace either the caller's
+// (use_static = false) or the library's static device array (use_static =
+// true: attn_fwd_ex_noalloc, which passes no workspace).
 int fwd_ex_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
                 int Nq, int Nk, int d, const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q,
                 int total_k, int causal, int window_left, int window_right, float alpha, int dtype,
-                int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes, const char* what,
-                void* stream) {
+                int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes, bool use_static,
+                const char* what, void* stream) {
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16)
     return fail(ATTN_ERR_UNSUPPORTED, "dtype %d is not supported (0 = bf16, 1 = f16)", dtype);
   if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0)
@@ -232,6 +236,22 @@ int fwd_ex_impl(const void* q, const void* k, const void* v, void* o, float* lse
   const int64_t qb = (int64_t)total_q * Hq * d * 2, kb = (int64_t)total_k * Hkv * d * 2;
   const int64_t lb = (int64_t)total_q * Hq * 4;
   const int64_t ws_need = nsplit > 1 ? attn_splitkv_workspace_bytes(nsplit, total_q, Hq, d) : 0;
+  if (use_static) {
+    if (ws_need > attn::kStaticWorkspaceBytes)
+      return fail(ATTN_ERR_UNSUPPORTED,
+                  "%d key ranges need %lld bytes of split-KV workspace, more than the %lld-byte static "
+                  "workspace of %s (use fewer splits, or attn_fwd_ex with a caller workspace)",
+                  nsplit, (long long)ws_need, (long long)attn::kStaticWorkspaceBytes, what);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (ws_need > 0) {
+      void* p = nullptr;
+      const int e = attn::static_workspace(&p);
+      if (e != 0) return hip_status(e, "static workspace lookup");
+      workspace = static_cast<float*>(p);
+      workspace_bytes = attn::kStaticWorkspaceBytes;
+    }
+  }
   const void* in[3] = {q, k, v};
   const int64_t in_b[3] = {qb, kb, kb};
   for (int i = 0; i < 3; ++i) {
@@ -287,7 +307,16 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
                 int pack_gqa, int num_splits, float* workspace, int64_t workspace_bytes, void* stream) {
   return fwd_ex_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k, causal,
                      window_left, window_right, alpha, dtype, pack_gqa, num_splits, workspace, workspace_bytes,
-                     "attn_fwd_ex", stream);
+                     false, "attn_fwd_ex", stream);
+}
+
+int attn_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                        int Nq, int Nk, int d, const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q,
+                        int total_k, int causal, int window_left, int window_right, float alpha, int dtype,
+                        int pack_gqa, int num_splits, void* stream) {
+  return fwd_ex_impl(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, cu_seqlens_q, cu_seqlens_k, total_q, total_k, causal,
+                     window_left, window_right, alpha, dtype, pack_gqa, num_splits, nullptr, 0, true,
+                     "attn_fwd_ex_noalloc", stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

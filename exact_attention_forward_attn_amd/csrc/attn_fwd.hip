@@ -42,10 +42,42 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn_internal.h"
 #include "kernel_common.h"
 
+// The static split-KV workspace of attn_fwd_ex_noalloc: kStaticWorkspaceBytes
+// of device memory per GPU, for callers that cannot allocate. In host code
+// `scratch` names a host-side stand-in, never the device memory: host code
+// uses only the address hipGetSymbolAddress returns for it on each device.
+static __device__ __align__(256) float scratch[attn::kStaticWorkspaceBytes / 4];
+
 namespace attn {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int static_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
+}
+
 namespace fwd16 {
 
 using namespace attn::dev;

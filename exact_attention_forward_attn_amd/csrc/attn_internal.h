@@ -80,6 +80,16 @@ inline bool uses_decode_kernel(int Nq, int Hq, int Hkv, int d) {
   return d <= 128 && (int64_t)Nq * (Hq / Hkv) <= kDecodeRows;
 }
 
+// Bytes of the static split-KV workspace each GPU holds for
+// attn_fwd_ex_noalloc (a file-scope device array, resident from the first
+// call on a device until the process ends).
+constexpr int64_t kStaticWorkspaceBytes = int64_t(16) << 20;
+
+// Device address of the current device's static workspace, looked up once
+// per device (hipGetSymbolAddress; allocates nothing). Returns 0 or a
+// hipError_t value.
+int static_workspace(void** ptr);
+
 // Each returns 0 on success or a hipError_t value.
 int launch_fwd_16(const FwdArgs& a, void* stream);
 int launch_decode_16(const FwdArgs& a, void* stream);

@@ -36,7 +36,9 @@
  *            N = 0 is a valid no-op. Nothing is printed, no exception
  *            crosses the ABI.
  *   State    the library keeps no state between calls except the
- *            thread-local error message; it allocates no device memory.
+ *            thread-local error message; it allocates no device memory
+ *            (attn_fwd_ex_noalloc uses a static device array instead of a
+ *            caller workspace).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -265,6 +267,34 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
  * num_splits <= 1): num_splits * total_q * Hq * (d + 1) * 4. */
 int64_t attn_splitkv_workspace_bytes(int num_splits, int total_q, int Hq, int d);
 
+/*
+ * attn_fwd_ex_noalloc -- attn_fwd_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without workspace / workspace_bytes.
+ * With several key ranges the range states go to a static device array the
+ * library holds on each GPU (ATTN_STATIC_WORKSPACE_BYTES = 16 MiB, resident
+ * from the first such call on that GPU until the process ends); the call
+ * itself allocates nothing (no hipMalloc, no hipFree).
+ *
+ *   Limit    attn_splitkv_workspace_bytes(ranges used, total_q, Hq, d) must
+ *            be <= ATTN_STATIC_WORKSPACE_BYTES, else ATTN_ERR_UNSUPPORTED
+ *            (checked before any launch). One range needs no workspace.
+ *   Sharing  every call on one GPU uses that GPU's single array, which keeps
+ *            the last call's contents (nothing in it needs to start at
+ *            zero: each range writes its whole state before the combine
+ *            reads it). Calls that overlap in time on one GPU (on different
+ *            streams, or from different threads) race on it; callers must
+ *            order them (one stream, or events).
+ *   Device   the array of the current device (hipGetDevice) is used; the
+ *            stream must belong to that device.
+ *   Result   identical to attn_fwd_ex with the same arguments (same kernels).
+ */
+#define ATTN_STATIC_WORKSPACE_BYTES (16 << 20)
+int attn_fwd_ex_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        const int* cu_seqlens_q, const int* cu_seqlens_k, int total_q, int total_k,
+                        int causal, int window_left, int window_right, float alpha, int dtype,
+                        int pack_gqa, int num_splits, void* stream);
 
 /* 1 if packing the query heads of a group takes fewer 128-row query tiles
  * than one head per tile (e.g. decode with Nq = 1 and Hq > Hkv), else 0. */

@@ -340,3 +340,42 @@ def test_binding_has_no_cpu_fallback(monkeypatch):
     monkeypatch.setattr(ea, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ea.load()
+
+
+def _fwd_noalloc(**kw):
+    lib = ea.load()
+    a = dict(q=FAKE, k=FAKE + 0x10000000, v=FAKE + 0x20000000, o=FAKE + 0x30000000, lse=FAKE + 0x40000000,
+             B=1, Hq=32, Hkv=32, Nq=64, Nk=8192, d=256, cu_q=None, cu_k=None, total_q=0, total_k=0, causal=0,
+             wl=-1, wr=-1, alpha=0.1, dtype=0, pack=-1, splits=128, stream=None)
+    a.update(kw)
+    return lib.attn_fwd_ex_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                   a["Nk"], a["d"], a["cu_q"], a["cu_k"], a["total_q"], a["total_k"], a["causal"],
+                                   a["wl"], a["wr"], a["alpha"], a["dtype"], a["pack"], a["splits"], a["stream"])
+
+
+def test_noalloc_rejects_split_state_beyond_the_static_workspace():
+    # 128 ranges x 64 rows x 32 heads x (256 + 1) floats = 269 MB > 16 MiB:
+    # refused before the static array is looked up or anything launched
+    assert ea.STATIC_WORKSPACE_BYTES == 16 << 20
+    need = ea.attn_splitkv_workspace_bytes(128, 64, 32, 256)
+    assert need > ea.STATIC_WORKSPACE_BYTES
+    assert _fwd_noalloc() == ea.ATTN_ERR_UNSUPPORTED
+    msg = ea.attn_last_error()
+    assert "static workspace" in msg and str(need) in msg and str(ea.STATIC_WORKSPACE_BYTES) in msg
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(Hkv=3), ea.ATTN_ERR_INVALID_ARG, "multiple of Hkv"),
+    (dict(splits=0), ea.ATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(q=None, splits=1), ea.ATTN_ERR_INVALID_ARG, "q is null"),
+    (dict(o=FAKE + 0x100, splits=1), ea.ATTN_ERR_INVALID_ARG, "o overlaps q"),
+])
+def test_noalloc_validates_like_attn_fwd_ex(kw, status, msg):
+    assert _fwd_noalloc(**kw) == status
+    assert msg in ea.attn_last_error()
+
+
+def test_noalloc_empty_problems_are_no_ops():
+    assert _fwd_noalloc(Nq=0) == ea.ATTN_OK
+    assert _fwd_noalloc(B=0) == ea.ATTN_OK
