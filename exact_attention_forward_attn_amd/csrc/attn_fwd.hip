@@ -265,15 +265,28 @@ void fwd_kernel(KernelArgs a) {
   const float c = a.c;
   // m_run: the exponent reference (a running max); msc = m_run * c (0 while
   // m_run = -inf).
-  // lacc: the sum of the rounded P that entered P V, accumulated by the
-  // matrix core as ones^T P^T next to O^T (every row holds the lane's query
-  // sum; it normalises O); l_lse: float32 sum of P (gives LSE).
+  // lsum: the sum of the rounded P that entered P V (it normalises O),
+  // accumulated by the matrix core with the 16x16x32 MFMA, one per 16-key P
+  // operand. That MFMA reads a lane's 8 P values as contraction rows
+  // 8 (l / 16) .. + 7 of column l % 16, so column n gathers lanes n, n + 16,
+  // n + 32, n + 48: queries n (lanes n, n + 32, row groups 0 and 2) and
+  // n + 16 (lanes n + 16, n + 48, groups 1 and 3). The A operand `sel`
+  // picks, for output rows m with m % 8 < 4, groups 0 and 2, and for the
+  // others groups 1 and 3. Lane l receives rows 4 (l / 16) .. + 3 of
+  // column l % 16, and that row choice lands exactly on its own query
+  // l % 32: every register of lsum holds the lane's query sum, and the
+  // lane's rho rescales it. l_lse: float32 sum of the unrounded P (gives
+  // LSE), this lane's half of its query's keys.
   float m_run = -__builtin_inff(), msc = 0.f;
-  f32x16 lacc = {};
+  f32x4 lsum = {};
   float l_lse = 0.f;
-  v8 ones;
+  v8 sel;
+  {
+    // lane l holds row m = l % 16 of A over contraction group l / 16
+    const T one = (T)((((lane >> 2) ^ (lane >> 4)) & 1) == 0 ? 1.0f : 0.0f);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (T)1.0f;
+    for (int e = 0; e < 8; ++e) sel[e] = one;
+  }
 
   // Keys of this workgroup: its key range [kb0, kb1), cut to the keys some
   // query of the workgroup sees. In the masked instantiation query n sees
@@ -381,15 +394,17 @@ void fwd_kernel(KernelArgs a) {
   // most the lane's float32 sum of its tile, so a sum <= 2^kTau proves the
   // rule held (a reference still at -inf always takes the update, which sets
   // it to the row maximum). O~ is normalised by the sum of the
-  // rounded p that entered P V (lacc), so O is an exact convex combination
-  // of the weights the product used; l_lse is the float32 sum (gives LSE).
+  // rounded p that entered P V (lsum), so O is an exact convex
+  // combination of the weights the product used; l_lse is the float32 sum
+  // (gives LSE).
   //
   // The work is cut into single VALU instructions placed on the steps of a
   // block (one MFMA each) so that no instruction waits on the one just
   // before it: score e has its fma at step f(e), its exp at f(e)+1, its
   // float32 add and 16-bit pack at f(e)+2. The sum uses two independent
-  // partials. (The sum of the rounded p is left to the
-  // matrix core: a v_dot2 next to an MFMA in flight waits for it to finish.)
+  // partials. (The sum of the rounded p is left to the matrix core: adding
+  // the rounded pairs on the VALU costs as much as the products it saves,
+  // and a v_dot2 next to an MFMA in flight waits for that MFMA to finish.)
   constexpr int NV = 16 * KB;  // scores per lane in a tile
   float fv[NV];
   float r32p[2], r32v;
@@ -460,7 +475,7 @@ void fwd_kernel(KernelArgs a) {
       For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<SB>{}, k, Int<1>{}, FalseT{}); });
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= rho;
-      lacc *= rho;
+      lsum *= rho;
       l_lse *= rho;
     }
     l_lse += r32v;
@@ -492,7 +507,7 @@ void fwd_kernel(KernelArgs a) {
         constexpr int kc = m / KB, kb = m % KB;
         return *(const v8*)(kt + kb * 32 * G::ROWB + (kc / 8) * 256 + kofs[kc % 8]);
       } else if constexpr (m - MQK >= DB * KB * 2) {
-        return ones;
+        return sel;
       } else {
         constexpr int t = m - MQK;
         constexpr int db = t / (2 * KB), kb = (t / 2) % KB, ks = t % 2;
@@ -514,7 +529,7 @@ void fwd_kernel(KernelArgs a) {
           oacc[db] = E::mfma(op, pk[J][kb][ks], oacc[db]);
         } else {
           constexpr int u = t - DB * KB * 2;
-          lacc = E::mfma(op, pk[J][u / 2][u % 2], lacc);
+          lsum = E::mfma16(op, pk[J][u / 2][u % 2], lsum);
         }
       }
     };
@@ -589,7 +604,7 @@ void fwd_kernel(KernelArgs a) {
   }  // nt > 0
 
   // ---- finalize and epilogue ------------------------------------------------
-  const float lt = lacc[0];
+  const float lt = lsum[0];
   const float ll = halves_sum(l_lse);
   const bool ok = lt > 0.f;  // false for 0 and NaN
   const float inv = ok ? 1.0f / lt : 0.f;

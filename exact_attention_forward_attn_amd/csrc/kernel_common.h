@@ -172,6 +172,15 @@ struct Elt<__bf16> {
     const v2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
   }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // the two halves of a packed pair widened exactly to float32: a bf16 is
+  // the top 16 bits of the float32 with the same value (one shift, one and)
+  static __device__ __forceinline__ float lo(v2 x) { return __uint_as_float(__builtin_bit_cast(uint32_t, x) << 16); }
+  static __device__ __forceinline__ float hi(v2 x) {
+    return __uint_as_float(__builtin_bit_cast(uint32_t, x) & 0xFFFF0000u);
+  }
 };
 
 template <>
@@ -194,6 +203,12 @@ struct Elt<_Float16> {
     const v2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(x, one, acc, false);
   }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // the two halves of a packed pair widened exactly to float32
+  static __device__ __forceinline__ float lo(v2 x) { return (float)x[0]; }
+  static __device__ __forceinline__ float hi(v2 x) { return (float)x[1]; }
 };
 
 // Geometry of the K/V tiles in LDS for head dimension D.
