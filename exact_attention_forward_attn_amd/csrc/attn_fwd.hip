@@ -132,8 +132,8 @@ constexpr int kWavesPerEU = D == 256 ? 1 : D == 128 ? ATTN_D128_WAVES : 2;
 //
 // LDS holds two K and two V tiles. K runs two tiles ahead of V: block i
 // reads V_i and K_{i+2} while V_{i+1} and K_{i+3} are copied in.
-template <int D, int KB, bool CAUSAL, typename T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>, kWavesPerEU<D>)))
+template <int D, int KB, int NW, bool CAUSAL, typename T>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>, kWavesPerEU<D>)))
 void fwd_kernel(KernelArgs a) {
   // The body is device code only; the host pass just needs the launch stub
   // (instantiating the body there makes clang drop the stub silently).
@@ -144,7 +144,9 @@ void fwd_kernel(KernelArgs a) {
   typedef typename E::v2 v2;
   typedef Geo<D, KB> G;
   constexpr int BN = G::BN;
-  constexpr int BM = 128;             // query rows per workgroup (32 per wave)
+  constexpr int BM = 32 * NW;         // query rows per workgroup (32 per wave)
+  constexpr int SPW = G::SEGS / NW;   // 1 KiB copy segments per wave and tile
+  static_assert(G::SEGS % NW == 0, "a tile must split evenly over the waves");
   constexpr int KC = D / 16;          // k-steps of the QK^T product
   constexpr int KCL = KC < 8 ? KC : 8;
   constexpr int DB = D / 32;          // 32-dim blocks of O
@@ -224,18 +226,18 @@ void fwd_kernel(KernelArgs a) {
   const int diag = n_i + off + a.win_r - 4 * h32;
 
   // ---- per-lane LDS offsets -------------------------------------------------
-  // global -> LDS copy: segment seg = wave + 4t, lane i covers row seg*RPS +
+  // global -> LDS copy: segment seg = wave + NW t, lane i covers row seg*RPS +
   // i/CPR, chunk i%CPR. The swizzles depend on the row modulo 16 (K) or 4 (V);
   // a step of t moves the row by 4*RPS, which keeps both except for K rows of
   // 512 bytes (RPS = 2), where the parity of t matters. So one per-lane base
   // (two for that K case) plus a uniform per-segment stride covers all t.
-  constexpr int KGP = (G::RPS * 4) % 16 == 0 ? 1 : 2;
+  constexpr int KGP = (G::RPS * NW) % 16 == 0 ? 1 : 2;
   uint32_t kg[KGP], vg0;
 #pragma unroll
   for (int t = 0; t < KGP; ++t) {
-    const int r = (wave + 4 * t) * G::RPS + lane / G::CPR;
+    const int r = (wave + NW * t) * G::RPS + lane / G::CPR;
     const int pc = lane % G::CPR;
-    kg[t] = (uint32_t)r * RSK + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * 4 * G::RPS * RSK;
+    kg[t] = (uint32_t)r * RSK + (uint32_t)((pc ^ swz_k<D>(r)) << 4) - (uint32_t)t * NW * G::RPS * RSK;
   }
   {
     const int r = wave * G::RPS + lane / G::CPR;
@@ -333,9 +335,9 @@ void fwd_kernel(KernelArgs a) {
     const uint32_t g0 = is_k ? kg[0] : vg0;
     const uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
 #pragma unroll
-    for (int t = 0; t < G::SEG_PER_WAVE; ++t) {
-      const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * 4 * G::RPS * RSK);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + 4 * t) * 1024), 16, voff, 0, 0, 0);
+    for (int t = 0; t < SPW; ++t) {
+      const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * NW * G::RPS * RSK);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + NW * t) * 1024), 16, voff, 0, 0, 0);
     }
   };
   // Workgroup barrier. Every LDS read of this wave has landed first (the
@@ -725,9 +727,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
 }
 
-template <int D, int KB, bool CAUSAL, typename T>
+template <int D, int KB, int NW, bool CAUSAL, typename T>
 int launch(const FwdArgs& f, hipStream_t st) {
-  constexpr int BM = 128;
+  constexpr int BM = 32 * NW;
   KernelArgs a;
   a.q = f.q; a.k = f.k; a.v = f.v; a.o = f.o; a.lse = f.lse;
   a.opart = f.opart; a.lpart = f.lpart;
@@ -746,7 +748,7 @@ int launch(const FwdArgs& f, hipStream_t st) {
   a.win_r = f.win_r;
   a.c = f.scale_log2;
   const int grid = a.n_mblk * a.nunit * a.nsplit;
-  hipLaunchKernelGGL((fwd_kernel<D, KB, CAUSAL, T>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((fwd_kernel<D, KB, NW, CAUSAL, T>), dim3(grid), dim3(64 * NW), 0, st, a);
   return (int)hipGetLastError();
 }
 
@@ -772,11 +774,27 @@ int launch_combine(const FwdArgs& f, hipStream_t st) {
 #ifndef ATTN_D256_KB
 #define ATTN_D256_KB 1
 #endif
+// Waves per workgroup (32 query rows each), non-causal and causal grids.
+#ifndef ATTN_D64_NW
+#define ATTN_D64_NW 4
+#endif
+#ifndef ATTN_D128_NW
+#define ATTN_D128_NW 4
+#endif
+#ifndef ATTN_D64_NW_CAUSAL
+#define ATTN_D64_NW_CAUSAL 4
+#endif
+#ifndef ATTN_D128_NW_CAUSAL
+#define ATTN_D128_NW_CAUSAL 4
+#endif
 
 template <int D, typename T>
 int dispatch_d(const FwdArgs& f, hipStream_t st) {
   constexpr int KB = D == 64 ? ATTN_D64_KB : D == 128 ? ATTN_D128_KB : ATTN_D256_KB;
-  return f.causal ? launch<D, KB, true, T>(f, st) : launch<D, KB, false, T>(f, st);
+  // one wave per SIMD at d = 256: a workgroup has at most 4 waves
+  constexpr int NW = D == 64 ? ATTN_D64_NW : D == 128 ? ATTN_D128_NW : 4;
+  constexpr int NWC = D == 64 ? ATTN_D64_NW_CAUSAL : D == 128 ? ATTN_D128_NW_CAUSAL : 4;
+  return f.causal ? launch<D, KB, NWC, true, T>(f, st) : launch<D, KB, NW, false, T>(f, st);
 }
 
 template <typename T>
