@@ -9,9 +9,16 @@ Prints ONE JSON line (metric, value, roofline, cpu_baseline, ...). Extra
 measurements (the sequence-length sweep, FP8) go to stderr, and to a JSON
 file when --out is given.
 
+The line also carries the parity of the timed output (the cpu_baseline leg
+runs the oracle on whole heads of the same inputs and compares them), the
+build provenance, and the headline kernel's MFMA utilisation, clock and HBM
+traffic from the rocprofv3 counters recorded in profiles/ for the current
+kernel source (null once the source changes).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8] [--bwd] [--decode]
        python bench.py --copy-calibration   (plain copy kernel for PMC scaling)
        python bench.py --gemm-ceiling       (dense bf16 GEMM reference, torch.matmul)
+       python bench.py --ingest-pmc DIR...  (rocprofv3 counter CSVs -> profiles/ summaries)
 """
 from __future__ import annotations
 
@@ -32,7 +39,14 @@ METRIC = "attention fwd TFLOPS + % of MFMA peak, bf16 d=128 N=8k (and fp8)"
 HEADLINE = dict(B=2, N=8192, H=16, d=128, causal=False)
 DECODE = dict(B=8, Hq=64, Hkv=8, Nk=8192, d=128)  # one new token, GQA 8:1, 8192-key cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_d128_n8192.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_attn_fwd_bf16_d128_n8192.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_forward_attn_amd", "csrc", "attn_fwd.hip")
+# the headline kernel (d=128, 32-key tiles, four waves, non-causal, bf16) as
+# rocprofv3 names it: mangled in counter CSVs, demangled in kernel traces
+HEADLINE_KERNEL = "fwd_kernel<128, 1, 4, false, __bf16>"
+HEADLINE_KERNEL_MANGLED = "10fwd_kernelILi128ELi1ELi4ELb0EDF16bE"
+# bf16 parity bounds of the forward (max |O - O_ref|, RMSE(O), max |LSE - LSE_ref|)
+PARITY_BOUNDS = {"max_abs": 1e-2, "rmse": 3e-3, "lse_abs": 1e-3}
 
 
 def compulsory_bytes(B, N, H, d):
@@ -103,9 +117,21 @@ def mall_flush():
     _FLUSH_BUF.max()
 
 
-def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
+def headline_inputs(B, N, H, d):
+    """The headline's Q, K, V from the shared seeded generator: the device
+    tensors (the exact bf16 bits) and the same numbers widened to float64
+    on the host, which the cpu_baseline leg feeds to the oracle."""
+    import numpy as np
     import torch
-    q, k, v = device_inputs(B, N, H, d)
+    from synth_inputs import make_qkv
+    bits, vals = make_qkv(B, N, H, d, seed=0)
+    dev = [torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16) for b in bits]
+    return dev, vals
+
+
+def bench_bf16(ea, B, N, H, d, causal, steps, warmup, inputs=None):
+    import torch
+    q, k, v = inputs if inputs is not None else device_inputs(B, N, H, d)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fn = lambda: ea.attn_fwd(q, k, v, o, lse, causal=causal)
@@ -113,6 +139,7 @@ def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
     per_ms = sum(per) / len(per)
     tf = flops(B, N, H, d, causal) / (per_ms * 1e-3) / 1e12
     r = {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "ms_total": total,
+         "ms_median": sorted(per)[len(per) // 2],
          "TFLOPS": tf, "frac_peak": tf / PEAK_TFLOPS["bf16"],
          "hbm_GBs": compulsory_bytes(B, N, H, d) / (per_ms * 1e-3) / 1e9}
     if causal:
@@ -124,6 +151,9 @@ def bench_bf16(ea, B, N, H, d, causal, steps, warmup):
         r["ms_cold"] = msc
         r["hbm_GBs_cold"] = compulsory_bytes(B, N, H, d) / (msc * 1e-3) / 1e9
         r["hbm_frac_cold"] = r["hbm_GBs_cold"] / PEAK_HBM_GBS
+    if inputs is not None:
+        # the timed launches' output (every launch writes the same bits)
+        r["_out"] = (o, lse)
     return r
 
 
@@ -207,13 +237,15 @@ def bench_fp8(ea, B, N, H, d, causal, steps, warmup):
             "frac_peak": tf / PEAK_TFLOPS["fp8"], "prepare_ms_per_tensor": sum(pper) / len(pper)}
 
 
-def cpu_baseline(target_s=15.0):
+def cpu_baseline(vals, out=None, target_s=15.0):
     """Times the float64 oracle on the host on a bounded sample of the
-    headline workload: whole (b, h) heads (all N query rows, all keys) until
-    ~target_s seconds are spent; reports TFLOP/s with the same FLOP count."""
+    headline workload: whole (b, h) heads of the headline's own inputs (all
+    N query rows, all keys), in order, until ~target_s seconds are spent;
+    reports TFLOP/s with the same FLOP count. When `out` holds the timed
+    launches' (O, LSE), each oracle head is also compared with the GPU's
+    (outside the timed regions of both)."""
     import numpy as np
     from oracle.attention import attention_head
-    from synth_inputs import make_qkv
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -221,21 +253,37 @@ def cpu_baseline(target_s=15.0):
         threads = os.cpu_count() or 1
     cfg = HEADLINE
     B, N, H, d = cfg["B"], cfg["N"], cfg["H"], cfg["d"]
-    # inputs of the first head only: the other heads are identical in cost
-    _, (q, k, v) = make_qkv(1, N, 1, d, seed=0)
-    heads = 0
-    t0 = time.perf_counter()
-    while True:
-        attention_head(q[0, :, 0], k[0, :, 0], v[0, :, 0], 1 / math.sqrt(d), cfg["causal"])
+    q, k, v = vals
+    o_gpu = lse_gpu = None
+    if out is not None:
+        o_gpu = out[0].float().cpu().numpy()
+        lse_gpu = out[1].cpu().numpy()
+    heads, el = 0, 0.0
+    sq = mx = lmx = 0.0
+    n_el = 0
+    while heads < B * H and el < target_s:
+        b, h = divmod(heads, H)
+        t0 = time.perf_counter()
+        o_ref, l_ref = attention_head(q[b, :, h], k[b, :, h], v[b, :, h], 1 / math.sqrt(d), cfg["causal"])
+        el += time.perf_counter() - t0
         heads += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or heads >= B * H:
-            break
+        if o_gpu is not None:
+            diff = o_gpu[b, :, h].astype(np.float64) - o_ref
+            sq += float(np.sum(diff ** 2))
+            n_el += diff.size
+            mx = max(mx, float(np.abs(diff).max()))
+            lmx = max(lmx, float(np.abs(lse_gpu[b, h].astype(np.float64) - l_ref).max()))
     per_head_flops = flops(1, N, 1, d, cfg["causal"])
     tf = heads * per_head_flops / el / 1e12
-    return {"value": tf, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} of {B * H} (b,h) heads at N={N}, d={d}, full rows, numpy float64 "
-                      f"({el:.1f} s); rate extrapolates linearly over heads"}
+    res = {"value": tf, "unit": "TFLOP/s", "cores": int(threads), "cpu_count": os.cpu_count(), "kind": "oracle",
+           "sample": f"{heads} of {B * H} (b,h) heads of the headline inputs at N={N}, d={d}, full rows, numpy "
+                     f"float64 ({el:.1f} s); rate extrapolates linearly over heads"}
+    if o_gpu is not None:
+        par = {"heads": heads, "elements": n_el, "max_abs": mx, "rmse": math.sqrt(sq / n_el), "lse_abs": lmx,
+               "bounds": PARITY_BOUNDS}
+        par["ok"] = all(par[k] <= PARITY_BOUNDS[k] for k in PARITY_BOUNDS)
+        res["parity"] = par
+    return res
 
 
 def traffic_entry():
@@ -246,6 +294,98 @@ def traffic_entry():
     if t.get("kernel_sha") != kernel_sha():
         return None
     return t.get("bytes_per_launch")
+
+
+def counters_entry():
+    """MFMA utilisation and the measured shader clock of the headline kernel,
+    from the rocprofv3 counters recorded for the current kernel source (None
+    once the source has changed since they were taken)."""
+    try:
+        c = json.load(open(COUNTERS_FILE))
+    except Exception:
+        return None
+    if c.get("kernel_sha") != kernel_sha():
+        return None
+    return {k: c[k] for k in ("mfma_busy", "clock_GHz", "mfma_per_tile", "valu_per_tile", "lds_per_tile",
+                              "kernel_us", "kernel_sha", "source") if k in c}
+
+
+def is_headline(kernel_name):
+    return HEADLINE_KERNEL in kernel_name or HEADLINE_KERNEL_MANGLED in kernel_name
+
+
+def ingest_pmc(dirs, out_counters=COUNTERS_FILE, out_traffic=TRAFFIC_FILE, commands=None):
+    """Reads rocprofv3 counter CSVs (one directory per --pmc run) and writes
+    the headline kernel's counter summary (MFMA busy, clock, instructions per
+    tile) and, when FETCH_SIZE / WRITE_SIZE and a copy calibration are among
+    them, its HBM traffic, each keyed to the kernel source hash.
+
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE per XCD);
+    clock = GRBM_GUI_ACTIVE per XCD / kernel time (from the same CSV's
+    start/end timestamps)."""
+    import csv
+    import glob
+    h = HEADLINE
+    simds, xcds = 1024, 8
+    tiles = (h["N"] // 32) * (h["N"] // 32) * h["B"] * h["H"]  # 32-key tiles x 32-row waves
+    per = {}      # counter -> list of per-dispatch values (headline kernel)
+    copy = {}
+    dur = []
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows = list(csv.DictReader(open(f)))
+            seen = {}
+            for r in rows:
+                name = r.get("Kernel_Name", "")
+                key = (r["Dispatch_Id"], r["Counter_Name"])
+                seen[key] = seen.get(key, 0.0) + float(r["Counter_Value"])
+                if is_headline(name) and "Start_Timestamp" in r and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    dur.append((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3)
+            names = {r["Dispatch_Id"]: r.get("Kernel_Name", "") for r in rows}
+            for (disp, cname), val in seen.items():
+                kname = names[disp]
+                if is_headline(kname):
+                    per.setdefault(cname, []).append((int(disp), val))
+                elif "copyBuffer" in kname:
+                    copy.setdefault(cname, []).append(val)
+    mean = {}
+    for cname, lst in per.items():
+        lst.sort()
+        vals = [v for _, v in lst[1:]] or [v for _, v in lst]  # the dispatches after the first
+        mean[cname] = sum(vals) / len(vals)
+    sha = kernel_sha()
+    if "GRBM_GUI_ACTIVE" in mean and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+        cyc = mean["GRBM_GUI_ACTIVE"] / xcds
+        out = {"kernel": f"{HEADLINE_KERNEL} (bf16, d=128, N=8192, B=2, H=16, non-causal)", "kernel_sha": sha,
+               "source": os.path.relpath(out_counters, ROOT), "counters_per_dispatch": mean,
+               "mfma_busy": mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * cyc)}
+        if dur:
+            us = sorted(dur)[len(dur) // 2]
+            out["kernel_us"] = us
+            out["clock_GHz"] = cyc / (us * 1e3)
+        for cname, key in (("SQ_INSTS_MFMA", "mfma_per_tile"), ("SQ_INSTS_LDS", "lds_per_tile")):
+            if cname in mean:
+                out[key] = mean[cname] / tiles
+        if "SQ_INSTS_VALU" in mean and "SQ_INSTS_MFMA" in mean:
+            out["valu_per_tile"] = (mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"]) / tiles
+        out["tiles_per_dispatch"] = tiles
+        out["commands"] = commands or []
+        with open(out_counters, "w") as f:
+            json.dump(out, f, indent=1)
+        print("wrote", out_counters)
+    if "FETCH_SIZE" in mean and "WRITE_SIZE" in mean and "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
+        n = 1 << 30
+        fs = n / (sum(copy["FETCH_SIZE"]) / len(copy["FETCH_SIZE"]) * 1024)
+        ws = n / (sum(copy["WRITE_SIZE"]) / len(copy["WRITE_SIZE"]) * 1024)
+        t = {"kernel": f"{HEADLINE_KERNEL} (bf16, d=128, N=8192, B=2, H=16, non-causal)", "kernel_sha": sha,
+             "fetch_kib_per_dispatch": mean["FETCH_SIZE"], "write_kib_per_dispatch": mean["WRITE_SIZE"],
+             "copy_calibration": {"copy_bytes": n, "fetch_scale": fs, "write_scale": ws},
+             "bytes_per_launch": int(mean["FETCH_SIZE"] * 1024 * fs + mean["WRITE_SIZE"] * 1024 * ws),
+             "algorithmic_bytes_per_launch": int(compulsory_bytes(h["B"], h["N"], h["H"], h["d"])),
+             "commands": commands or []}
+        with open(out_traffic, "w") as f:
+            json.dump(t, f, indent=1)
+        print("wrote", out_traffic)
 
 
 def copy_calibration():
@@ -328,7 +468,16 @@ def main():
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--gemm-ceiling", action="store_true", help="time dense bf16 GEMMs (torch.matmul) and exit")
+    ap.add_argument("--ingest-pmc", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc output directories of the headline kernel (and of "
+                         "--copy-calibration) into the kernel-keyed counter / traffic files under profiles/, "
+                         "then exit (no GPU needed)")
+    ap.add_argument("--ingest-command", action="append", default=[],
+                    help="with --ingest-pmc: a command that produced the counters (recorded in the file)")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc, commands=args.ingest_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (attention heads and "
@@ -366,7 +515,9 @@ def main():
         return
 
     h = HEADLINE
-    head = bench_bf16(ea, h["B"], h["N"], h["H"], h["d"], h["causal"], args.steps, args.warmup)
+    dev, host_vals = headline_inputs(h["B"], h["N"], h["H"], h["d"])
+    head = bench_bf16(ea, h["B"], h["N"], h["H"], h["d"], h["causal"], args.steps, args.warmup, inputs=dev)
+    head_out = head.pop("_out")
     # the metric's "(and fp8)": the FP8 forward at the same shape, timed like
     # the headline right after it (prepare excluded, its time per tensor
     # reported beside)
@@ -427,9 +578,19 @@ def main():
     gemm = gemm_tflops(16384, 16384, 8192)
     log("gemm_ceiling", json.dumps({"gemm": "16384x16384x8192 bf16, N(0,1)", "TFLOPS": gemm}))
 
-    cpu = None if args.no_cpu else cpu_baseline()
+    # the oracle on the host cores, on whole heads of the same inputs; it also
+    # checks the timed launches' output head by head
+    cpu = None if args.no_cpu else cpu_baseline(host_vals, head_out)
+    parity = cpu.pop("parity", None) if cpu else None
     if cpu:
         log("cpu_baseline", json.dumps(cpu))
+        log("parity", json.dumps(parity))
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        rocm = None
+    build = {"library": ea.load().attn_version().decode(), "rocm": rocm, "torch": torch.__version__,
+             "hip_runtime": getattr(torch.version, "hip", None)}
 
     fl = flops(h["B"], h["N"], h["H"], h["d"], h["causal"])
     achieved = fl / (head["ms"] * 1e-3) / 1e12
@@ -458,7 +619,11 @@ def main():
                                                     "nominal clock)",
                                            "TFLOPS": round(gemm, 1), "frac": round(achieved / gemm, 4)}},
         "cpu_baseline": cpu,
+        "parity": parity,
+        "build": build,
     }
+    line["roofline"]["counters"] = counters_entry()
+    line["ms_median"] = round(head["ms_median"], 5)
     line["fp8"] = {"value": round(f8["TFLOPS"], 2), "unit": "TFLOP/s", "peak": PEAK_TFLOPS["fp8"],
                    "frac": round(f8["TFLOPS"] / PEAK_TFLOPS["fp8"], 4), "ms": round(f8["ms"], 5),
                    "prepare_ms_per_tensor": round(f8["prepare_ms_per_tensor"], 5),

@@ -22,6 +22,13 @@ ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fp8.hip", "attn_bwd.hip", "attn_decode.hip"]
 
+# The compiler the kernels were validated with (parity suite green on the
+# MI355X). The decode kernel issues its K loads in inline assembly that the
+# compiler's wait counting does not see, and the FP8 kernel pads one MFMA
+# result read by hand; both rely on this compiler's code generation, so a
+# different hipcc gets a warning (the GPU parity tests are the gate).
+VALIDATED_HIP = "7.2.26015"
+
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
     f"-I{INCLUDE}", f"-I{CSRC}",
@@ -44,6 +51,29 @@ def _hipcc():
     raise RuntimeError("hipcc not found")
 
 
+def _run(cmd, cwd=None):
+    try:
+        p = subprocess.run(cmd, cwd=cwd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True, timeout=60)
+        return p.stdout.strip() if p.returncode == 0 else ""
+    except (OSError, subprocess.SubprocessError):
+        return ""
+
+
+def build_info(hipcc):
+    """Provenance compiled into attn_version(): the source commit (with
+    "+dirty" for uncommitted changes), the HIP compiler and the ROCm release."""
+    commit = _run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT) or "unknown"
+    if commit != "unknown" and _run(["git", "status", "--porcelain", "--untracked-files=no"], cwd=ROOT):
+        commit += "+dirty"
+    ver = _run([hipcc, "--version"])
+    hip = next((l.split(":", 1)[1].strip() for l in ver.splitlines() if l.startswith("HIP version")), "unknown")
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        rocm = "unknown"
+    return {"commit": commit, "hip": hip, "rocm": rocm, "arch": ARCH}
+
+
 def _compile(args):
     cmd, src = args
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -53,6 +83,11 @@ def _compile(args):
 
 def build(verbose: bool = False, out: str = LIB) -> str:
     hipcc = _hipcc()
+    info = build_info(hipcc)
+    if not info["hip"].startswith(VALIDATED_HIP):
+        print(f"warning: hipcc {info['hip']} differs from the validated {VALIDATED_HIP}; "
+              "run the GPU parity tests before trusting this build", file=sys.stderr)
+    info_def = "-DATTN_BUILD_INFO=\"commit {commit}, hip {hip}, rocm {rocm}, {arch}\"".format(**info)
     tmp = tempfile.mkdtemp(prefix="attn_build_")
     try:
         jobs = []
@@ -65,7 +100,7 @@ def build(verbose: bool = False, out: str = LIB) -> str:
                 extra = [] if src in NO_VGPR_FORM else VGPR_FORM
                 cmd = [hipcc, *HIP_FLAGS, *extra, *COMMON, "-c", path, "-o", obj]
             else:
-                cmd = [hipcc, *COMMON, "-x", "c++", "-c", path, "-o", obj]
+                cmd = [hipcc, *COMMON, info_def, "-x", "c++", "-c", path, "-o", obj]
             jobs.append((cmd, src))
         with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
             results = list(ex.map(_compile, jobs))

@@ -526,6 +526,9 @@ int attn_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o, float*
 
 const char* attn_last_error(void) { return g_err.c_str(); }
 
-const char* attn_version(void) { return "attn-gfx950 0.1"; }
+#ifndef ATTN_BUILD_INFO
+#define ATTN_BUILD_INFO "unknown build"
+#endif
+const char* attn_version(void) { return "attn-gfx950 0.2 (" ATTN_BUILD_INFO ")"; }
 
 }  // extern "C"

@@ -342,7 +342,8 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const void* o, cons
  * stays valid until the next call on the same thread. */
 const char* attn_last_error(void);
 
-/* Library version string. */
+/* Library version string: "attn-gfx950 <version> (commit <c>, hip <v>, rocm
+ * <r>, <arch>)", the provenance recorded when the library was built. */
 const char* attn_version(void);
 
 #ifdef __cplusplus
