@@ -644,18 +644,56 @@ void fwd_kernel(KernelArgs a) {
         const int64_t li = a.cu_q ? (int64_t)hq_e * a.total_q + qrow : ((int64_t)b * a.Hq + hq_e) * a.Nq + ne;
         a.lse[li] = lse;
       }
-      T* orow = (T*)a.o + (qrow * a.Hq + hq_e) * D;
+    }
+  }
+  if (a.nsplit <= 1) {
+    // O goes out through LDS: the accumulator gives a lane 4 consecutive
+    // dims of its row at a 32-byte stride, so stored directly each
+    // instruction would write 16 bytes into each of 32 rows. Written to LDS
+    // as [32 rows][D] (16-byte chunk index XOR the row, so the 32 rows of a
+    // write land on different banks) and read back row-wise, every store
+    // instruction writes 64 / (D / 8) whole rows. The wave's 32 x D area is
+    // carved from the K/V slots, free once every wave has passed its last
+    // block (the barrier; a workgroup that saw no key has issued no copy).
+    constexpr int CPR = D / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;  // rows per store instruction
+    constexpr int OW = 32 * D * 2;  // bytes of one wave's area
+    constexpr bool IN_SLOTS = NW * OW <= 4 * G::TILE && G::TILE % OW == 0;
+    // (eight-wave workgroups at d = 128 need more than the slots hold)
+    __shared__ __attribute__((aligned(1024))) char oextra[IN_SLOTS ? 16 : NW * OW];
+    char* ow;
+    if constexpr (IN_SLOTS) {
+      barrier();
+      // the slots are four separate objects: wave w's area starts at byte
+      // w * OW of the sequence kbuf0, kbuf1, vbuf0, vbuf1
+      const int byte = wave * OW, slot = byte / G::TILE, within = byte - slot * G::TILE;
+      ow = (slot == 0 ? kbuf0 : slot == 1 ? kbuf1 : slot == 2 ? vbuf0 : vbuf1) + within;
+    } else {
+      ow = oextra + wave * OW;
+    }
+    const int rl = lane_e & 31, hl = lane_e >> 5;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          typedef T t4 __attribute__((ext_vector_type(4)));
-          f4 f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        f4 f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * q4 + e] * inv;
-          t4 ov = __builtin_convertvector(f, t4);
-          *(u32x2*)(orow + db * 32 + 8 * q4 + 4 * h32) = __builtin_bit_cast(u32x2, ov);
-        }
+        for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * q4 + e] * inv;
+        const t4 ov = __builtin_convertvector(f, t4);
+        *(u32x2*)(ow + rl * (2 * D) + (((4 * db + q4) ^ (rl & (CPR - 1))) << 4) + 8 * hl) = __builtin_bit_cast(u32x2, ov);
+      }
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane_e / CPR, cc = lane_e % CPR;
+      const u32x4 val = *(const u32x4*)(ow + r * (2 * D) + ((cc ^ (r & (CPR - 1))) << 4));
+      const int qr = qw + r;
+      if (qr < rows) {
+        const int nr = pack ? qr / grp : qr;
+        const int hr = pack ? hu * grp + (qr - nr * grp) : hu;
+        *(u32x4*)((T*)a.o + (((int64_t)q_row0 + nr) * a.Hq + hr) * D + 8 * cc) = val;
+      }
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
