@@ -673,12 +673,23 @@ void fwd8_kernel(Fwd8Args a) {
   const float lt = halves_sum(l_run);
   const bool ok = lt > 0.f;
   const float inv = ok ? (nsb ? 1.f : dvt[0]) / lt : 0.f;
-  if (qi < N) {
-    if (h32 == 0) {
-      const float lse = ok ? (m_run + __builtin_amdgcn_logf(lt) - kOff8) * kLn2 : -__builtin_inff();
-      a.lse[(int64_t)bh * N + qi] = lse;
-    }
-    __bf16* orow = a.o + head_off + (int64_t)qi * a.H * D;
+  if (qi < N && h32 == 0) {
+    const float lse = ok ? (m_run + __builtin_amdgcn_logf(lt) - kOff8) * kLn2 : -__builtin_inff();
+    a.lse[(int64_t)bh * N + qi] = lse;
+  }
+  // O through LDS, as in the 16-bit kernel: each wave's 32 x D bf16 tile is
+  // written to the K/V slots (free after the barrier) as [32 rows][D] with
+  // the 16-byte chunk index XOR the row, and read back row-wise, so each
+  // store instruction writes 64 / (D / 8) whole rows instead of 16 bytes
+  // into each of 32 rows.
+  {
+    constexpr int CPR = D / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;  // rows per store instruction
+    constexpr int OW = 32 * D * 2;
+    static_assert(4 * OW <= 4 * G::TILE && G::TILE % OW == 0, "the K/V slots hold the workgroup's O tile");
+    barrier();
+    const int byte = wave * OW, slot = byte / G::TILE, within = byte - slot * G::TILE;
+    char* ow = (slot == 0 ? kbuf0 : slot == 1 ? kbuf1 : slot == 2 ? vbuf0 : vbuf1) + within;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -686,9 +697,17 @@ void fwd8_kernel(Fwd8Args a) {
         f32x4 f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) f[e] = oacc[db][4 * g + e] * inv;
-        bf16x4 ov = __builtin_convertvector(f, bf16x4);
-        *(u32x2*)(orow + db * 32 + 8 * g + 4 * h32) = __builtin_bit_cast(u32x2, ov);
+        const bf16x4 ov = __builtin_convertvector(f, bf16x4);
+        *(u32x2*)(ow + l32 * (2 * D) + (((4 * db + g) ^ (l32 & (CPR - 1))) << 4) + 8 * h32) =
+            __builtin_bit_cast(u32x2, ov);
       }
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane / CPR, cc = lane % CPR;
+      const u32x4 val = *(const u32x4*)(ow + r * (2 * D) + ((cc ^ (r & (CPR - 1))) << 4));
+      const int qr = qw + r;
+      if (qr < N) *(u32x4*)(a.o + head_off + (int64_t)qr * a.H * D + 8 * cc) = val;
+    }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
