@@ -23,10 +23,10 @@ ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_fp8.hip", "attn_bwd.hip", "attn_decode.hip"]
 
 # The compiler the kernels were validated with (parity suite green on the
-# MI355X). The decode kernel issues its K loads in inline assembly that the
-# compiler's wait counting does not see, and the FP8 kernel pads one MFMA
-# result read by hand; both rely on this compiler's code generation, so a
-# different hipcc gets a warning (the GPU parity tests are the gate).
+# MI355X). The FP8 kernel pads the read of its last MFMA results by hand
+# (this compiler spaced that read one wait state short), which relies on
+# this compiler's code generation, so a different hipcc gets a warning (the
+# GPU parity tests are the gate).
 VALIDATED_HIP = "7.2.26015"
 
 COMMON = [

@@ -90,23 +90,6 @@ __device__ __forceinline__ int swz_val(int r) {
   return D == 64 ? (((r >> 1) & 3) << 1) : ((r & 7) << 1);
 }
 
-// 16-byte buffer load whose completion the compiler does not track: the
-// caller waits for it with an explicit s_waitcnt vmcnt and then passes the
-// value through pin(). (With the builtin load the compiler's own waits,
-// which cannot follow the two-tile ring across the loop, drain every load
-// before each tile.) desc is the raw buffer descriptor: base address, range
-// in bytes (reads past it return 0), flags.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFF), (int)bytes, 0x00020000};
-}
-__device__ __forceinline__ u32x4 load16_untracked(const i32x4& desc, uint32_t voff) {
-  u32x4 r;
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(r) : "v"(voff), "s"(desc) : "memory");
-  return r;
-}
-
 template <typename T>
 struct Mfma16;
 template <>
@@ -166,21 +149,20 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
   const uint32_t RSK = (uint32_t)a.Hkv * D * 2;
   const int64_t q_off = ((int64_t)q_row0 * a.Hq + (int64_t)hk * g) * D;
   const int64_t k_off = ((int64_t)k_row0 * a.Hkv + hk) * D;
-  const i32x4 dq = make_desc((const T*)a.q + q_off, (uint32_t)(len_q - 1) * RSQ + (uint32_t)g * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + q_off, (uint32_t)(len_q - 1) * RSQ + (uint32_t)g * D * 2);
   const uint32_t kspan = len_k > 0 ? (uint32_t)(len_k - 1) * RSK + D * 2 : 0;
-  const i32x4 dk = make_desc((const T*)a.k + k_off, kspan);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + k_off, kspan);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + k_off, kspan);
 
   // Q^T operands: lane holds row l16, dims 32 kc + 8 grp + 0..7 (zero past
-  // the unit's rows through the buffer range check); the wait for the first
-  // tile covers them (issued before it)
+  // the unit's rows through the buffer range check)
   const int n_r = l16 / g;  // query index of this lane's row
   v8 qreg[KC];
   {
     const uint32_t qo = (uint32_t)n_r * RSQ + (uint32_t)(l16 - n_r * g) * D * 2 + grp * 16;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      qreg[kc] = __builtin_bit_cast(v8, load16_untracked(dq, qo + kc * 64));
+      qreg[kc] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rq, qo + kc * 64, 0, 0));
   }
 
   // ---- key range and this wave's tiles ---------------------------------------
@@ -225,7 +207,7 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
         kreg[ST][kb * KC + kc] = __builtin_bit_cast(
-            v8, load16_untracked(dk, (uint32_t)(kv0 + 16 * kb + l16) * RSK + (uint32_t)(64 * kc + 16 * grp)));
+            v8, __builtin_amdgcn_raw_buffer_load_b128(rk, (uint32_t)(kv0 + 16 * kb + l16) * RSK + (uint32_t)(64 * kc + 16 * grp), 0, 0));
     char* dst = stage(st_tag);
 #pragma unroll
     for (int ii = 0; ii < G::INSTR; ++ii) {
@@ -239,14 +221,12 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
 
   auto step = [&](auto st_tag, int i) ATTN_INLINE {
     constexpr int ST = decltype(st_tag)::value;
+    // tile i's V copy has landed (tile i+1's may be in flight); the compiler
+    // adds the waits for the K and Q registers itself
     if (i + 1 < cnt)
-      wait_vmcnt<G::PER_TILE>();  // tile i landed; tile i+1 may be in flight
+      wait_vmcnt<G::PER_TILE>();
     else
       wait_vmcnt<0>();
-#pragma unroll
-    for (int j = 0; j < 2 * KC; ++j) pin(kreg[ST][j]);  // K (and Q) are read after the wait
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) pin(qreg[kc]);
     const LDS_AS char* vt = (const LDS_AS char*)stage(st_tag);
     const int kv0 = kb0 + (t0 + wave + NW * i) * G::BN;
 
@@ -315,12 +295,6 @@ __global__ __launch_bounds__(DGeo<D>::NW * 64) void decode_kernel(Args a) {
 
   if (cnt > 0) issue(Int<0>{}, 0);
   if (cnt > 1) issue(Int<1>{}, 1);
-  if (cnt == 0) {
-    // no tile: still let the Q loads land while their registers are live
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) pin(qreg[kc]);
-  }
   // unrolled by two so the K buffer and ring stage indices are constants
   for (int i = 0; i < cnt; i += 2) {
     step(Int<0>{}, i);
