@@ -73,8 +73,12 @@ def test_large_scores_stay_finite(gpu):
     o_ref, l_ref = attention(qf, kf, vf, 1 / math.sqrt(128), True)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     err = errors(o, o_ref, lse, l_ref)
-    assert err["max_abs"] <= 2e-2 and err["rmse"] <= 3e-3, err
-    assert err["lse_abs"] <= 2e-3 * max(1.0, np.abs(l_ref).max() / 100), err
+    # Rows this peaked select single V entries, |O| up to ~4.5, and rounding
+    # O to bf16 alone costs up to half an ulp, 2^-8 |O| (0.0176 at 4.5), more
+    # than the flat 1e-2: the bound is that plus 1e-3 for the kernel.
+    bound = 2.0 ** -8 * float(np.abs(o_ref).max()) + 1e-3
+    assert err["max_abs"] <= bound and err["rmse"] <= 3e-3, (err, bound)
+    assert err["lse_abs"] <= 1e-3, err
 
 
 def test_repeated_launches_are_bitwise_identical(gpu):
