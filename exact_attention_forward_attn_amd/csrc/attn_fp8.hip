@@ -72,9 +72,11 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Round-to-nearest-even e4m3 codes of (a, b, c, d) after saturation, packed
-// little-endian in one 32-bit word.
+// little-endian in one 32-bit word. The first conversion writes the low half
+// and keeps the high half of its third operand, which the second one then
+// overwrites: any word serves there, and a's own bits need no extra register.
 __device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }
