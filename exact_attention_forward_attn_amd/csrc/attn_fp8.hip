@@ -270,6 +270,8 @@ struct Fwd8Args {
   int n_mblk;
   int nsb;        // descale blocks per (b, head): ceil(N/128), or 0 for per-tensor
   float c;        // alpha * log2(e)
+  // division constants of n_mblk, B * H, H and H / Hkv
+  FastDiv fd_mblk, fd_bh, fd_h, fd_g;
 };
 
 // Exponent offset (the pages' Max_offset) and rescale threshold of the lazy
@@ -328,11 +330,10 @@ void fwd8_kernel(Fwd8Args a) {
   const int h32 = lane >> 5;
   const int l32 = lane & 31;
 
-  const int BH = a.B * a.H;
   int mblk, bh;
-  decode_block(blockIdx.x, a.n_mblk, BH, CAUSAL, mblk, bh);
-  const int b = bh / a.H;
-  const int hh = bh % a.H;
+  decode_block((uint32_t)blockIdx.x, a.fd_mblk, a.fd_bh, CAUSAL, mblk, bh);
+  const int b = (int)fdiv((uint32_t)bh, a.fd_h);
+  const int hh = bh - b * a.H;
   const int N = a.N;
   const int q0 = mblk * BM;
   const int qw = q0 + wave * 32;
@@ -342,7 +343,7 @@ void fwd8_kernel(Fwd8Args a) {
   const uint32_t span = (uint32_t)(N - 1) * RS + D;
   // grouped heads ("FlashAttention-3 on Hopper", section 5.6.1): the
   // key/value head of query head hh, and its row stride
-  const int hk = hh / (a.H / a.Hkv);
+  const int hk = (int)fdiv((uint32_t)hh, a.fd_g);
   const uint32_t RSK = (uint32_t)a.Hkv * D;
   const int64_t kv_off = ((int64_t)b * N * a.Hkv + hk) * D;
   const uint32_t span_kv = (uint32_t)(N - 1) * RSK + D;
@@ -639,10 +640,18 @@ void fwd8_kernel(Fwd8Args a) {
   if (n_masked > 0) apply_mask(Int<0>{}, (nt - 1) * BN);
   if (n_masked > 1) apply_mask(Int<1>{}, (nt - 2) * BN);
   {
+    // The first tile always sets the reference (it starts at -inf): the row
+    // maximum first, then P in one pass; O~ and l are still zero.
     tile_scalars(Int<0>{});
-    constexpr Sched S0{8};
-    For<0, S0.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<8>{}, TrueT{}); });
-    finish_tile(Int<0>{});
+    float mx = s[0][0][0];
+#pragma unroll
+    for (int e = 1; e < NV; ++e) mx = __builtin_fmaxf(mx, s[0][e / 16][e % 16]);
+    m_run = halves_max(mx) * ct;
+    ot = (m_run == -__builtin_inff() ? 0.f : -m_run) + kOff8;
+    constexpr Sched S1{1};
+    For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<1>{}, FalseT{}); });
+    ev[0] = nsb ? (int)((__float_as_uint(dvt[0]) >> 23) & 0xFFu) : 127;
+    l_run = r32v;
   }
 
   auto iteration = [&](int i, auto j_tag, auto qk_tag, auto sm_tag) ATTN_INLINE {
@@ -726,6 +735,10 @@ int launch_fwd(const FwdArgs& f, hipStream_t st) {
   a.n_mblk = (f.N + BM - 1) / BM;
   a.nsb = f.block_rows ? (f.N + f.block_rows - 1) / f.block_rows : 0;
   a.c = f.scale_log2;
+  a.fd_mblk = make_fastdiv(a.n_mblk);
+  a.fd_bh = make_fastdiv(f.B * f.H);
+  a.fd_h = make_fastdiv(f.H);
+  a.fd_g = make_fastdiv(f.H / a.Hkv);
   const int grid = a.n_mblk * f.B * f.H;
   hipLaunchKernelGGL((fwd8_kernel<D, CAUSAL>), dim3(grid), dim3(256), 0, st, a);
   return (int)hipGetLastError();

@@ -109,6 +109,8 @@ struct KernelArgs {
   int nsplit, split_len;
   int win_l, win_r;   // window widths (masked kernels; wide = unbounded)
   float c;            // alpha * log2(e)
+  // division constants of n_mblk, nunit * nsplit, nsplit, hu and g
+  FastDiv fd_mblk, fd_bh, fd_split, fd_hu, fd_g;
 };
 
 // Waves per SIMD each kernel is compiled for (its register budget).
@@ -173,11 +175,13 @@ void fwd_kernel(KernelArgs a) {
   // group (the KV head of query head h is floor(h / g), "FlashAttention-3 on
   // Hopper", section 5.6.1).
   int mblk, rest;
-  decode_block(blockIdx.x, a.n_mblk, a.nunit * a.nsplit, CAUSAL, mblk, rest);
-  const int unit = rest / a.nsplit;
+  decode_block((uint32_t)blockIdx.x, a.fd_mblk, a.fd_bh, CAUSAL, mblk, rest);
+  const int unit = (int)fdiv((uint32_t)rest, a.fd_split);
   const int split = rest - unit * a.nsplit;
-  const int b = unit / a.hu;
+  const int b = (int)fdiv((uint32_t)unit, a.fd_hu);
   const int hu = unit - b * a.hu;
+  // x / g for the non-negative row and head indices below
+  auto gdiv = [&](int x) ATTN_INLINE { return (int)fdiv((uint32_t)x, a.fd_g); };
   const int grp = a.g;
   const bool pack = a.pack != 0;
   // rows of this batch entry in q/o and k/v; offsets of packed batches are
@@ -197,9 +201,9 @@ void fwd_kernel(KernelArgs a) {
   if (q0 >= rows) return;  // past a short sequence (uniform over the workgroup)
   const int qw = q0 + wave * 32;              // first tile row of this wave
   const int qi = qw + l32;                    // this lane's tile row
-  const int n_i = pack ? qi / grp : qi;       // its query index
+  const int n_i = pack ? gdiv(qi) : qi;       // its query index
   const int hq_i = pack ? hu * grp + (qi - n_i * grp) : hu;  // its query head
-  const int hk = pack ? hu : hu / grp;
+  const int hk = pack ? hu : gdiv(hu);
   const int off = len_k - len_q;              // causal offset (bottom-right)
   const uint32_t RSQ = (uint32_t)a.Hq * D * 2;   // bytes between query rows
   const uint32_t RSK = (uint32_t)a.Hkv * D * 2;  // bytes between key rows
@@ -300,8 +304,8 @@ void fwd_kernel(KernelArgs a) {
   const int kb1 = min(len_k, kb0 + a.split_len);
   int kv_end = kb1, kbase = kb0;
   if (CAUSAL) {
-    const int n_first = pack ? q0 / grp : q0;
-    const int n_last = min(len_q - 1, pack ? (q0 + BM - 1) / grp : q0 + BM - 1);
+    const int n_first = pack ? gdiv(q0) : q0;
+    const int n_last = min(len_q - 1, pack ? gdiv(q0 + BM - 1) : q0 + BM - 1);
     kv_end = min(kv_end, n_last + off + a.win_r + 1);
     const int lo = n_first + off - a.win_l;  // first key the workgroup sees
     if (lo > kb0) kbase = kb0 + (min(lo, kb1) - kb0) / BN * BN;
@@ -315,9 +319,9 @@ void fwd_kernel(KernelArgs a) {
   int jm = kb1 - kbase >= BN ? (kb1 - kbase - BN) / BN + 1 : 0;
   int left_from = nt;
   if (CAUSAL) {
-    const int x = (pack ? qw / grp : qw) + off + a.win_r - kbase - BN + 1;
+    const int x = (pack ? gdiv(qw) : qw) + off + a.win_r - kbase - BN + 1;
     jm = min(jm, x >= 0 ? x / BN + 1 : 0);
-    const int lw = (pack ? (qw + 31) / grp : qw + 31) + off - a.win_l;  // the wave's last left bound
+    const int lw = (pack ? gdiv(qw + 31) : qw + 31) + off - a.win_l;  // the wave's last left bound
     if (lw > kbase) left_from = max(0, nt - (lw - kbase + BN - 1) / BN);
   }
   const int n_masked = max(0, nt - jm);
@@ -567,9 +571,17 @@ void fwd_kernel(KernelArgs a) {
   if (n_masked > 0 || left_from == 0) apply_mask(Int<0>{}, kbase + (nt - 1) * BN);
   if (nt > 1 && (n_masked > 1 || left_from <= 1)) apply_mask(Int<1>{}, kbase + (nt - 2) * BN);
   {
-    constexpr Sched S0{16};
-    For<0, S0.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<16>{}, TrueT{}); });
-    finish_tile(Int<0>{});
+    // The first tile always moves the reference (it starts at -inf), so it
+    // takes the row maximum directly and P in one pass; O~ and the sums are
+    // still zero, so nothing is rescaled.
+    float mx = s[0][0][0];
+#pragma unroll
+    for (int e = 1; e < NV; ++e) mx = __builtin_fmaxf(mx, s[0][e / 16][e % 16]);
+    m_run = halves_max(mx);
+    msc = (m_run == -__builtin_inff()) ? 0.f : m_run * c;
+    constexpr Sched S1{1};
+    For<0, S1.last() + 1>::run([&](auto k) ATTN_INLINE { sm_step(Int<0>{}, k, Int<1>{}, FalseT{}); });
+    l_lse = r32v;
   }
 
   // iteration i: V_i and K_{i+2} have landed (copied during iteration i-1)
@@ -616,7 +628,7 @@ void fwd_kernel(KernelArgs a) {
   int lane_e;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
   const int qi_e = qw + (lane_e & 31);
-  const int ne = pack ? qi_e / grp : qi_e;
+  const int ne = pack ? gdiv(qi_e) : qi_e;
   const int hq_e = pack ? hu * grp + (qi_e - ne * grp) : hu;
   if (qi_e < rows) {
     const float lse = ok ? (m_run * c + __builtin_amdgcn_logf(ll)) * kLn2 : -__builtin_inff();
@@ -690,7 +702,7 @@ void fwd_kernel(KernelArgs a) {
       const u32x4 val = *(const u32x4*)(ow + r * (2 * D) + ((cc ^ (r & (CPR - 1))) << 4));
       const int qr = qw + r;
       if (qr < rows) {
-        const int nr = pack ? qr / grp : qr;
+        const int nr = pack ? gdiv(qr) : qr;
         const int hr = pack ? hu * grp + (qr - nr * grp) : hu;
         *(u32x4*)((T*)a.o + (((int64_t)q_row0 + nr) * a.Hq + hr) * D + 8 * cc) = val;
       }
@@ -785,6 +797,11 @@ int launch(const FwdArgs& f, hipStream_t st) {
   a.win_l = f.win_l;
   a.win_r = f.win_r;
   a.c = f.scale_log2;
+  a.fd_mblk = make_fastdiv(a.n_mblk);
+  a.fd_bh = make_fastdiv(a.nunit * a.nsplit);
+  a.fd_split = make_fastdiv(a.nsplit);
+  a.fd_hu = make_fastdiv(a.hu);
+  a.fd_g = make_fastdiv(a.g);
   const int grid = a.n_mblk * a.nunit * a.nsplit;
   hipLaunchKernelGGL((fwd_kernel<D, KB, NW, CAUSAL, T>), dim3(grid), dim3(64 * NW), 0, st, a);
   return (int)hipGetLastError();

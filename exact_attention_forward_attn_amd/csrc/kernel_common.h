@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
+
 namespace attn {
 namespace dev {
 
@@ -111,6 +113,26 @@ __device__ __forceinline__ void decode_block(int w, int n_mblk, int BH, bool cau
     const int L = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + kk;
     mblk = L % n_mblk;
     bh = L / n_mblk;
+  }
+}
+
+// The same mapping with the two sizes as launch-time division constants
+// (scalar multiply-high instead of the float-reciprocal division sequence).
+__device__ __forceinline__ void decode_block(uint32_t w, const FastDiv& n_mblk, const FastDiv& BH, bool causal, int& mblk,
+                                             int& bh) {
+  uint32_t q, r;
+  if (causal) {
+    fdivmod(w, BH, q, r);
+    mblk = (int)(n_mblk.d - 1 - q);
+    bh = (int)r;
+  } else {
+    const uint32_t nblk = n_mblk.d * BH.d;
+    const uint32_t per = nblk >> 3, rem = nblk & 7;
+    const uint32_t x = w & 7, kk = w >> 3;
+    const uint32_t L = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + kk;
+    fdivmod(L, n_mblk, q, r);
+    mblk = (int)r;
+    bh = (int)q;
   }
 }
 
