@@ -278,12 +278,12 @@ struct Fwd8Args {
 // path, in base-2 units: a score at most kTau8 above the reference gives
 // p <= 2^(kOff8 + kTau8) = 2^8.8 < 448, the e4m3 maximum. The pages shift by
 // 8 against the exact running max; with a lazy reference the same bound can
-// be split as 8 + 0.8 or 5 + 3.8. The second split re-does a tile only when
-// one of the wave's rows sees its max rise by 3.8 (a 0.8 rise was common
-// enough that about 30% of tiles were computed twice), and P still reaches up
-// to 2^8.8.
-constexpr float kOff8 = 5.0f;
-constexpr float kTau8 = 3.8f;
+// be split as 8 + 0.8, 5 + 3.8 or 4 + 4.8. A larger tau re-does fewer tiles
+// (with 8 + 0.8 about 30% of tiles were computed twice; the re-done tile's
+// maximum then gets p = 2^kOff8 exactly, which keeps peaked rows accurate),
+// and P still reaches up to 2^8.8.
+constexpr float kOff8 = 4.0f;
+constexpr float kTau8 = 4.8f;
 static_assert(kOff8 + kTau8 <= 8.807f, "p must stay below the e4m3 maximum 448");
 // The common path tests the rule on the lane's float32 sum of its tile's p
 // (computed anyway for l): every p is at most that sum, so a sum of at most
