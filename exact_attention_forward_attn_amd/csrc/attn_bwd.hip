@@ -114,6 +114,11 @@ __device__ __forceinline__ void seq_extent(const KernelArgs& a, int b, int& q_ro
   }
 }
 
+// LDS reads in flight ahead of the MFMAs of the pipelined dK/dV step
+#ifndef ATTN_BWD_RING
+#define ATTN_BWD_RING 4
+#endif
+
 // waves per SIMD each kernel is compiled for (its register budget): dK/dV
 // keeps K, V, dK^T and dV^T in registers
 template <int D>
@@ -495,56 +500,88 @@ void dkdv_kernel(KernelArgs a) {
       f32x4 l2c[4], dlc[4];
       read_rows(slot_r(Int<J>{}), l2c, dlc);
       f32x16 sn = f32x16{}, dpn = f32x16{};
-      float pv[16], dsv[16];
+      float pv[16], dsv[16], xv[16], dd[16];
+      // -LSE log2(e) of the tile's rows (the exponent's addend)
+      f32x4 nl[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) nl[g] = l2c[g] * -kLog2e;
       int q0t, jcur;
       tile_of(u, q0t, jcur);
       const int kb = band_base(q0t);
-      // operand ring: the LDS read of MFMA m + 2 is issued at step m
-      v8 ring[2];
+      // operand ring: the LDS read of MFMA m + RL is issued at step m
+      constexpr int RL = ATTN_BWD_RING;
+      v8 ring[RL];
       auto opnd = [&](auto m_tag) ATTN_INLINE -> v8 {
         constexpr int m = decltype(m_tag)::value;
         return m < KC ? row_op<D, T>(to, qn, m) : row_op<D, T>(to, on, m - KC);
       };
-      if constexpr (NEXT) {
-        ring[0] = opnd(Int<0>{});
-        ring[1] = opnd(Int<1>{});
-      }
+      if constexpr (NEXT) For<0, (RL < NM ? RL : NM)>::run([&](auto m) ATTN_INLINE { ring[decltype(m)::value] = opnd(m); });
       For<0, NM>::run([&](auto m_tag) ATTN_INLINE {
         constexpr int m = decltype(m_tag)::value;
         if constexpr (NEXT) {
           if constexpr (m < KC)
-            sn = E::mfma(ring[m % 2], kreg[m], sn);
+            sn = E::mfma(ring[m % RL], kreg[m], sn);
           else
-            dpn = E::mfma(ring[m % 2], vreg[m - KC], dpn);
-          if constexpr (m + 2 < NM) ring[m % 2] = opnd(Int<m + 2>{});
+            dpn = E::mfma(ring[m % RL], vreg[m - KC], dpn);
+          if constexpr (m + RL < NM) ring[m % RL] = opnd(Int<m + RL>{});
         }
-        // p and dS of the scores assigned to this step
-        For<(m * 16) / NM, ((m + 1) * 16) / NM>::run([&](auto r_tag) ATTN_INLINE {
+        // p and dS of score r, skewed over three steps so that no VALU
+        // instruction waits on the one before it: the exponent and dP - D
+        // at step f(r), the exp at f(r) + 1, the mask and dS at f(r) + 2
+        For<0, 16>::run([&](auto r_tag) ATTN_INLINE {
           constexpr int r = decltype(r_tag)::value;
-          const float lse = l2c[r >> 2][r & 3];
-          // unmasked: the LSE = -inf select never fires (no row is without
-          // keys), but without it the register allocation of this
-          // instantiation spills
-          const bool ok = CAUSAL ? in_band(kb, r) : lse != -__builtin_inff();
-          const float p = ok ? exp2_fast(__builtin_fmaf(sc[r], c, -lse * kLog2e)) : 0.f;
-          pv[r] = p;
-          dsv[r] = p * (dpc[r] - dlc[r >> 2][r & 3]);
-          pin(dsv[r]);
+          constexpr int f = (r * (NM - 2)) / 16;
+          if constexpr (f == m) {
+            xv[r] = __builtin_fmaf(sc[r], c, nl[r >> 2][r & 3]);
+            pin(xv[r]);
+            dd[r] = dpc[r] - dlc[r >> 2][r & 3];
+            pin(dd[r]);
+          }
+          if constexpr (f + 1 == m) {
+            xv[r] = exp2_fast(xv[r]);
+            pin(xv[r]);
+          }
+          if constexpr (f + 2 == m) {
+            // unmasked: the LSE = -inf select never fires (no row is without
+            // keys), but without it the register allocation of this
+            // instantiation spills
+            const bool ok = CAUSAL ? in_band(kb, r) : l2c[r >> 2][r & 3] != -__builtin_inff();
+            const float p = ok ? xv[r] : 0.f;
+            pv[r] = p;
+            dsv[r] = p * dd[r];
+            pin(dsv[r]);
+          }
         });
         __builtin_amdgcn_sched_barrier(0);
       });
+      // dV^T and dK^T products of tile u, alternating (each accumulator is
+      // reused every other MFMA); their transposed operands come through a
+      // ring of R2 reads issued ahead, the first ones before P and dS are
+      // packed
+      const char* qc = slot_q(Int<J>{});
+      const char* oc = slot_o(Int<J>{});
+      constexpr int R2 = ATTN_BWD_RING;
+      constexpr int NM2 = 4 * DB;
+      auto opnd2 = [&](auto m_tag) ATTN_INLINE -> v8 {
+        constexpr int m = decltype(m_tag)::value;
+        return tr_op<D, T>(to, (m & 1) ? qc : oc, m / 4, (m / 2) % 2);
+      };
+      v8 ring2[R2];
+      For<0, (R2 < NM2 ? R2 : NM2)>::run([&](auto m) ATTN_INLINE { ring2[decltype(m)::value] = opnd2(m); });
       v8 pk[2], dk8[2];
       pack16<T>(pv, pk);
       pack16<T>(dsv, dk8);
-      const char* qc = slot_q(Int<J>{});
-      const char* oc = slot_o(Int<J>{});
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dvt[db] = E::mfma(tr_op<D, T>(to, oc, db, ks), pk[ks], dvt[db]);
-          dkt[db] = E::mfma(tr_op<D, T>(to, qc, db, ks), dk8[ks], dkt[db]);
-        }
+      __builtin_amdgcn_sched_barrier(0);
+      For<0, NM2>::run([&](auto m_tag) ATTN_INLINE {
+        constexpr int m = decltype(m_tag)::value;
+        constexpr int db = m / 4, ks = (m / 2) % 2;
+        if constexpr (m & 1)
+          dkt[db] = E::mfma(ring2[m % R2], dk8[ks], dkt[db]);
+        else
+          dvt[db] = E::mfma(ring2[m % R2], pk[ks], dvt[db]);
+        if constexpr (m + R2 < NM2) ring2[m % R2] = opnd2(Int<m + R2>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
       wait_vmcnt<0>();
       barrier_all();
       sc = sn;
