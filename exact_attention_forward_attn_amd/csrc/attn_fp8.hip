@@ -93,6 +93,29 @@ __device__ __forceinline__ float block_scale(float amax) {
   return __uint_as_float((b & 0x7F800000u) + ((b & 0x007FFFFFu) ? 0x00800000u : 0u));
 }
 
+// Value of lane (lane ^ LM) for LM < 16, through the DPP lane moves inside a
+// row of 16 lanes (no LDS round trip): xor 1 and 2 are quad permutations,
+// xor 8 is a rotation of the row by 8, and xor 4 takes the rotation by 12 or
+// by 4 depending on the lane's bit 2. li is the lane's index within its
+// (16-aligned) group. Wider partners go through the LDS permute.
+template <int LM>
+__device__ __forceinline__ float lane_xor(float v, int li) {
+  const int x = __float_as_int(v);
+  if constexpr (LM == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+  } else if constexpr (LM == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+  } else if constexpr (LM == 8) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, true));  // row_ror 8
+  } else if constexpr (LM == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0xF, true);  // row_ror 12: lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, true);  // row_ror 4: lane - 4
+    return __int_as_float((li & 4) ? dn : up);
+  } else {
+    return __shfl_xor(v, LM);
+  }
+}
+
 // MODE 0: per-block scales (block_rows = 128), writes codes and descales.
 // MODE 1: per-tensor amax pass (atomic max of the float bits into descale[0]).
 // MODE 2: per-tensor quantisation with amax read from descale[0].
@@ -102,6 +125,8 @@ template <int D, bool HAD, int MODE>
 __global__ __launch_bounds__(256) void prep_kernel(PrepKernelArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int LPR = D / 8;            // lanes per row
+  constexpr int LSTAGES = LPR == 8 ? 3 : LPR == 16 ? 4 : 5;  // log2(LPR)
+  static_assert((1 << LSTAGES) == LPR, "lanes per row");
   constexpr int RPI = 256 / LPR;        // rows per iteration of the workgroup
   constexpr int ITER = 128 / RPI;
   __shared__ float red[4];
@@ -145,17 +170,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKernelArgs a) {
             y[it][j + hs] = u - w;
           }
       }
-#pragma unroll
-      for (int hs = 8; hs < D; hs <<= 1) {
-        const int lm = hs / 8;
-        const bool lower = (li & lm) == 0;
+      // lane stages: the partner is lane li ^ lm; the lower lane of the pair
+      // keeps own + other, the upper one other - own (one FMA with a +-1)
+      For<0, LSTAGES>::run([&](auto st_tag) ATTN_INLINE {
+        constexpr int lm = 1 << decltype(st_tag)::value;
+        const float sg = (li & lm) ? -1.f : 1.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float own = y[it][j];
-          const float oth = __shfl_xor(own, lm);
-          y[it][j] = lower ? own + oth : oth - own;
+          y[it][j] = __builtin_fmaf(sg, own, lane_xor<lm>(own, li));
         }
-      }
+      });
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[it][j] *= sgn[j];
     }
