@@ -147,15 +147,24 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKernelArgs a) {
     }
   }
 
+  // buffer resources over this (b, h)'s rows: rows past N read as zero
+  // (which leaves the block amax unchanged) and their stores are dropped,
+  // so no lane takes a branch around its loads
+  const int64_t head0 = ((int64_t)b * a.N * a.H + h) * D;
+  const uint32_t span = (uint32_t)((int64_t)(a.N - 1) * rs + D);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + head0, span * 2);
+  const __amdgpu_buffer_rsrc_t rx8 = make_rsrc(a.x8 + head0, span);
   float y[ITER][8];
   float amax = 0.f;
+  u32x4 raw[ITER];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int n = blk * 128 + it * RPI + rsub;
-    const bool valid = n < a.N;
-    const __bf16* src = a.x + ((int64_t)b * a.N + (valid ? n : 0)) * rs + (int64_t)h * D + 8 * li;
-    u32x4 raw = valid ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
-    bf16x8 xv = __builtin_bit_cast(bf16x8, raw);
+    const uint32_t n = (uint32_t)(blk * 128 + it * RPI + rsub);
+    raw[it] = __builtin_amdgcn_raw_buffer_load_b128(rx, (n * (uint32_t)rs + 8 * li) * 2, 0, 0);
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    bf16x8 xv = __builtin_bit_cast(bf16x8, raw[it]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[it][j] = (float)xv[j];
     if (HAD) {
@@ -184,10 +193,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKernelArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[it][j] *= sgn[j];
     }
-    if (valid) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[it][j]));
-    }
+    for (int j = 0; j < 8; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(y[it][j]));
   }
 
   if (MODE == 0 || MODE == 1) {
@@ -203,18 +210,20 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKernelArgs a) {
   if (MODE == 2) amax = __uint_as_float(*(const volatile unsigned*)a.descale);
   const float scale = MODE == 0 ? block_scale(amax) : (amax > 0.f ? amax / 448.0f : 1.0f);
   if (MODE == 0 && threadIdx.x == 0) a.descale[(int64_t)bh * a.nblk + blk] = scale;
+  // A block scale is a power of two, so multiplying by its (exact)
+  // reciprocal rounds exactly like the division; the per-tensor scale
+  // amax / 448 is not, and is divided by.
+  const float inv = 1.0f / scale;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int n = blk * 128 + it * RPI + rsub;
-    if (n < a.N) {
-      float q[8];
+    const uint32_t n = (uint32_t)(blk * 128 + it * RPI + rsub);
+    float q[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = sat448(y[it][j] / scale);
-      u32x2 w;
-      w[0] = pack_e4m3(q[0], q[1], q[2], q[3]);
-      w[1] = pack_e4m3(q[4], q[5], q[6], q[7]);
-      *(u32x2*)(a.x8 + ((int64_t)b * a.N + n) * rs + (int64_t)h * D + 8 * li) = w;
-    }
+    for (int j = 0; j < 8; ++j) q[j] = sat448(MODE == 0 ? y[it][j] * inv : y[it][j] / scale);
+    u32x2 w;
+    w[0] = pack_e4m3(q[0], q[1], q[2], q[3]);
+    w[1] = pack_e4m3(q[4], q[5], q[6], q[7]);
+    __builtin_amdgcn_raw_buffer_store_b64(w, rx8, n * (uint32_t)rs + 8 * li, 0, 0);
   }
 #endif
 }
