@@ -207,12 +207,15 @@ def bench_decode(ea, B, Hq, Hkv, Nk, d, splits, steps, warmup):
 
 
 def hbm_read_ceiling():
-    """Plain streaming reads on this part: torch's max over 1 GiB (read-only)
-    and a 1 GiB device copy (read + write), with the MALL flushed first."""
+    """Plain streaming reads on this part: torch's float32 sum over 1 GiB
+    (read-only) and a 1 GiB device copy (read + write), with the MALL
+    flushed first. (A max over bytes is bound by its per-byte compares, not
+    by HBM.)"""
     import torch
     x = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
     y = torch.empty_like(x)
-    _, per = time_launches(lambda: x.max(), 10, 2, flush=mall_flush)
+    xf = x.view(torch.float32)
+    _, per = time_launches(lambda: xf.sum(), 10, 2, flush=mall_flush)
     ms_r = sum(per) / len(per)
     _, per = time_launches(lambda: y.copy_(x), 10, 2, flush=mall_flush)
     ms_c = sum(per) / len(per)
