@@ -135,3 +135,34 @@ def test_sweep_configs_sampled(gpu, d, H, N):
 
 def test_long_causal_sampled(gpu):
     check_sampled(gpu, 1, 32768, 16, 128, (True,), heads=2)
+
+
+def test_tensors_past_two_billion_elements(gpu):
+    """Each of Q, K, V, O holds 17 x 65536 x 16 x 128 = 2.28e9 elements, so
+    the last batch entries start past element 2^31 (64-bit offsets in the
+    kernel's row arithmetic). Inputs are drawn on the device by a seeded
+    torch generator and rounded to bf16; the oracle gets the same bf16
+    values for the sampled (b, h) slices and computes the sampled rows from
+    every key."""
+    import torch
+    from oracle.attention import attention_head
+    B, N, H, d = 17, 65536, 16, 128
+    g = torch.Generator(device="cuda").manual_seed(17)
+    q, k, v = [torch.randn((B, N, H, d), device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+               for _ in range(3)]
+    o, lse = gpu.attention(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    for b, h in ((0, 0), (16, 15), (16, 3)):
+        rows = np.array(sorted({0, 1, 31, 32, 40000, N - 2, N - 1} | set(rng.integers(0, N, 8).tolist())))
+        qf = q[b, :, h].float().cpu().numpy().astype(np.float64)
+        kf = k[b, :, h].float().cpu().numpy().astype(np.float64)
+        vf = v[b, :, h].float().cpu().numpy().astype(np.float64)
+        o_ref, l_ref = attention_head(qf, kf, vf, 1 / math.sqrt(d), True, rows=rows)
+        og = o[b, rows, h].float().cpu().numpy().astype(np.float64)
+        lg = lse[b, h, rows].cpu().numpy().astype(np.float64)
+        err = errors(og, o_ref, lg, l_ref)
+        print((b, h), err, flush=True)
+        assert_bf16_tolerances(err, ("2^31+", b, h))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
