@@ -253,3 +253,44 @@ def test_fp8_hadamard_beats_per_tensor_on_full_heads(gpu):
     print(res, flush=True)
     assert res["block+hadamard"] <= 3e-2, res
     assert res["block+hadamard"] < 0.75 * res["per-tensor"], res
+
+
+def test_fp8_tensors_past_two_billion_elements(gpu):
+    """Prepare and forward on tensors of 17 x 65536 x 16 x 128 = 2.28e9
+    elements (the last batch entries start past element 2^31): the codes of
+    sampled rows of the last entry equal the oracle's quantiser on the same
+    bf16 rows, and sampled outputs stay within the FP8 bound of the fp64
+    oracle on the unquantised inputs. Inputs come from a seeded torch
+    generator on the device."""
+    import torch
+    from oracle.attention import attention_head
+    B, N, H, d = 17, 65536, 16, 128
+    g = torch.Generator(device="cuda").manual_seed(23)
+    q, k, v = [torch.randn((B, N, H, d), device="cuda", generator=g, dtype=torch.float32).to(torch.bfloat16)
+               for _ in range(3)]
+    q8, sq = gpu.fp8_prepare(q, 128, True, 5)
+    k8, sk = gpu.fp8_prepare(k, 128, True, 5)
+    v8, sv = gpu.fp8_prepare(v, 128, False, 5)
+    o, lse = gpu.attention_fp8(q8, k8, v8, sq, sk, sv, causal=True, block_rows=128)
+    torch.cuda.synchronize()
+    # codes of one 128-row block of the last batch entry, head 15, bit for bit
+    b, h, blk = 16, 15, 511
+    rows = slice(128 * blk, 128 * blk + 128)
+    xk = k[b, rows, h].float().cpu().numpy()[None, :, None, :]
+    codes, desc = quantize(xk, 128, True, 5)
+    got = k8[b, rows, h].cpu().numpy()
+    assert np.array_equal(got, codes[0, :, 0, :])
+    assert float(sk[b, h, blk].cpu()) == float(desc[0, 0, 0])
+    rng = np.random.default_rng(23)
+    for b, h in ((0, 0), (16, 15)):
+        sel = np.array(sorted({1, 40000, N - 1} | set(rng.integers(1, N, 12).tolist())))
+        qf = q[b, :, h].float().cpu().numpy().astype(np.float64)
+        kf = k[b, :, h].float().cpu().numpy().astype(np.float64)
+        vf = v[b, :, h].float().cpu().numpy().astype(np.float64)
+        o_ref, l_ref = attention_head(qf, kf, vf, 1 / math.sqrt(d), True, rows=sel)
+        og = o[b, sel, h].float().cpu().numpy().astype(np.float64)
+        err = errors(og, o_ref)
+        print((b, h), err, flush=True)
+        assert err["rmse"] <= 3e-2, err
+    del q, k, v, q8, k8, v8, o, lse
+    torch.cuda.empty_cache()
