@@ -630,6 +630,9 @@ def main():
     line["fp8"] = {"value": round(f8["TFLOPS"], 2), "unit": "TFLOP/s", "peak": PEAK_TFLOPS["fp8"],
                    "frac": round(f8["TFLOPS"] / PEAK_TFLOPS["fp8"], 4), "ms": round(f8["ms"], 5),
                    "prepare_ms_per_tensor": round(f8["prepare_ms_per_tensor"], 5),
+                   # the three prepare passes (Q, K, V) plus the forward
+                   "end_to_end_TFLOPS": round(flops(h["B"], h["N"], h["H"], h["d"], h["causal"])
+                                              / ((f8["ms"] + 3 * f8["prepare_ms_per_tensor"]) * 1e-3) / 1e12, 2),
                    "config": "e4m3, power-of-two 128-row block scales + Hadamard on Q and K, inputs N(0,1) with 0.1% of "
                              "entries x10, d=128, N=8192, B=2, H=16, non-causal"}
     if args.out:
