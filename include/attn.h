@@ -142,7 +142,7 @@ int attn_fp8_prepare(const void* x, void* x8, float* descale,
  *
  * Scores are accumulated in float32 and multiplied by alpha * dq * dk per
  * tile; P is formed as exp2 of the score minus a reference that trails the
- * row maximum by at most 3.8, plus an offset of 5 (the pages' Max_offset,
+ * row maximum by at most 4.8, plus an offset of 4 (the pages' Max_offset,
  * lowered from 8 so that P <= 2^8.8 < 448 stays inside e4m3), rounded to
  * e4m3 for the P V product, which applies dv as the V operand's scale.
  */
