@@ -88,6 +88,7 @@ using namespace attn::dev;
 // rescale threshold of the lazy path, in base-2 exponent units
 constexpr float kTau = 8.0f;
 constexpr float kPmax = 256.0f;  // 2^kTau
+static_assert(kPmax == (float)(1 << (int)kTau), "kPmax must be 2^kTau");
 
 struct KernelArgs {
   const void* q;
@@ -235,7 +236,11 @@ void fwd_kernel(KernelArgs a) {
   // a step of t moves the row by 4*RPS, which keeps both except for K rows of
   // 512 bytes (RPS = 2), where the parity of t matters. So one per-lane base
   // (two for that K case) plus a uniform per-segment stride covers all t.
-  constexpr int KGP = (G::RPS * NW) % 16 == 0 ? 1 : 2;
+  // In general a step of t moves the row by RPS*NW, so K needs one base per
+  // residue of t modulo 16 / gcd(RPS*NW, 16).
+  constexpr int KSTEP = (G::RPS * NW) % 16;
+  constexpr int KGP = KSTEP == 0 ? 1 : KSTEP % 8 == 0 ? 2 : KSTEP % 4 == 0 ? 4 : 16;
+  static_assert((G::RPS * NW) % 4 == 0, "the V swizzle must repeat with the segment step");
   uint32_t kg[KGP], vg0;
 #pragma unroll
   for (int t = 0; t < KGP; ++t) {
@@ -336,11 +341,9 @@ void fwd_kernel(KernelArgs a) {
   // does not cover the scalar offset.)
   auto issue = [&](const __amdgpu_buffer_rsrc_t& rs, bool is_k, char* dst, int i) ATTN_INLINE {
     const uint32_t base = (uint32_t)(kbase + (nt - 1 - i) * BN) * RSK;
-    const uint32_t g0 = is_k ? kg[0] : vg0;
-    const uint32_t g1 = is_k ? kg[KGP - 1] : vg0;
 #pragma unroll
     for (int t = 0; t < SPW; ++t) {
-      const uint32_t voff = ((t & 1) ? g1 : g0) + (base + (uint32_t)t * NW * G::RPS * RSK);
+      const uint32_t voff = (is_k ? kg[t % KGP] : vg0) + (base + (uint32_t)t * NW * G::RPS * RSK);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + (wave + NW * t) * 1024), 16, voff, 0, 0, 0);
     }
   };
