@@ -30,7 +30,7 @@ from synth_inputs import make_dout, make_qkv_gqa
 
 pytestmark = pytest.mark.gpu
 
-N_CONFIGS = 60
+N_CONFIGS = 300
 
 
 def _draw(i):
@@ -143,7 +143,7 @@ def test_random_config(gpu, i):
 
 # ---- decode shapes: few query rows per KV head (the decode kernel) ----------
 
-N_DECODE = 30
+N_DECODE = 150
 
 
 def _draw_decode(i):
@@ -206,7 +206,7 @@ def test_random_decode(gpu, i):
 
 # ---- FP8: prepare + forward over random shapes and scale modes --------------
 
-N_FP8 = 20
+N_FP8 = 100
 
 
 @pytest.mark.parametrize("i", range(N_FP8))
