@@ -39,7 +39,7 @@ namespace bwd16 {
 
 using namespace attn::dev;
 
-constexpr float kLog2e = 1.4426950408889634f;
+[[maybe_unused]] constexpr float kLog2e = 1.4426950408889634f;  // device code only
 
 // ---- D = rowsum(dO o O) ------------------------------------------------------
 // rows in memory order r = row*H + h with row = b*N + n (dense) or the packed
