@@ -139,7 +139,7 @@ def bench_bf16(ea, B, N, H, d, causal, steps, warmup, inputs=None):
     per_ms = sum(per) / len(per)
     tf = flops(B, N, H, d, causal) / (per_ms * 1e-3) / 1e12
     r = {"B": B, "N": N, "H": H, "d": d, "causal": causal, "ms": per_ms, "ms_total": total,
-         "ms_median": sorted(per)[len(per) // 2],
+         "ms_median": sorted(per)[len(per) // 2], "ms_min": min(per), "ms_max": max(per),
          "TFLOPS": tf, "frac_peak": tf / PEAK_TFLOPS["bf16"],
          "hbm_GBs": compulsory_bytes(B, N, H, d) / (per_ms * 1e-3) / 1e9}
     if causal:
@@ -627,6 +627,9 @@ def main():
     }
     line["roofline"]["counters"] = counters_entry()
     line["ms_median"] = round(head["ms_median"], 5)
+    # spread of the K timed launches (each bracketed by its own HIP events)
+    line["ms_min"] = round(head["ms_min"], 5)
+    line["ms_max"] = round(head["ms_max"], 5)
     line["fp8"] = {"value": round(f8["TFLOPS"], 2), "unit": "TFLOP/s", "peak": PEAK_TFLOPS["fp8"],
                    "frac": round(f8["TFLOPS"] / PEAK_TFLOPS["fp8"], 4), "ms": round(f8["ms"], 5),
                    "prepare_ms_per_tensor": round(f8["prepare_ms_per_tensor"], 5),
