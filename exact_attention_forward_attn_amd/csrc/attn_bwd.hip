@@ -120,15 +120,16 @@ __device__ __forceinline__ void seq_extent(const KernelArgs& a, int b, int& q_ro
 #endif
 
 // waves per SIMD each kernel is compiled for (its register budget): dK/dV
-// keeps K, V, dK^T and dV^T in registers
+// keeps K, V, dK^T and dV^T in registers. At d = 64 both kernels fit three
+// waves (168 VGPRs each) without spilling.
 template <int D>
-constexpr int kWavesDkdv = D == 64 ? 2 : 1;
+constexpr int kWavesDkdv = D == 64 ? 3 : 1;
 // dK/dV kernels that run the software-pipelined loop (those at one wave per
 // SIMD, which have the registers for a second tile's S and dP)
 template <int D>
 constexpr bool kPipeDkdv = D == 128;
 template <int D>
-constexpr int kWavesDq = D == 256 ? 1 : 2;
+constexpr int kWavesDq = D == 256 ? 1 : D == 128 ? 2 : 3;
 
 // XOR swizzle of the 16-byte chunk index of row r of a backward tile. The
 // tiles are read two ways. Row-wise (ds_read_b128, the A operand of S or

@@ -114,12 +114,18 @@ struct KernelArgs {
   FastDiv fd_mblk, fd_bh, fd_split, fd_hu, fd_g;
 };
 
-// Waves per SIMD each kernel is compiled for (its register budget).
+// Waves per SIMD each kernel is compiled for (its register budget). At
+// d = 64 with 32-key tiles a wave needs about 150 VGPRs, so three fit (168
+// each): the third wave hides latency where the softmax's VALU work per MFMA
+// is highest.
 #ifndef ATTN_D128_WAVES
 #define ATTN_D128_WAVES 2
 #endif
+#ifndef ATTN_D64_WAVES
+#define ATTN_D64_WAVES 3
+#endif
 template <int D>
-constexpr int kWavesPerEU = D == 256 ? 1 : D == 128 ? ATTN_D128_WAVES : 2;
+constexpr int kWavesPerEU = D == 256 ? 1 : D == 128 ? ATTN_D128_WAVES : ATTN_D64_WAVES;
 
 // Software pipeline of one wave (tile i = i-th KV tile in processing order):
 //
@@ -824,7 +830,7 @@ int launch_combine(const FwdArgs& f, hipStream_t st) {
 
 // KV tile size per head dimension, in 32-key blocks.
 #ifndef ATTN_D64_KB
-#define ATTN_D64_KB 2
+#define ATTN_D64_KB 1
 #endif
 #ifndef ATTN_D128_KB
 #define ATTN_D128_KB 1
