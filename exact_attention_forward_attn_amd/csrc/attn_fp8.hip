@@ -492,16 +492,20 @@ void fwd8_kernel(Fwd8Args a) {
       s[SB][kb] = mfma8(ka, qreg[kc], kc == 0 ? f32x16{} : s[SB][kb]);
     }
   };
+  // Keys at lane offset o >= lim are masked (at or past N, or right of the
+  // diagonal). The sign of o - lim selects the score or -inf: no compare
+  // mask per element is kept live.
   auto apply_mask = [&](auto sb_tag, int kv0) ATTN_INLINE {
     constexpr int SB = decltype(sb_tag)::value;
     const int tn = N - kv0 - 4 * h32;
-    const int tc = qi - kv0 - 4 * h32;
+    const int lim = CAUSAL ? min(tn, qi - kv0 - 4 * h32 + 1) : tn;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
-        if (o >= tn || (CAUSAL && o > tc)) s[SB][kb][r] = -__builtin_inff();
+        const int vis = (o - lim) >> 31;  // all ones iff o < lim
+        s[SB][kb][r] = __int_as_float((__float_as_int(s[SB][kb][r]) & vis) | (int)(0xff800000u & ~(uint32_t)vis));
       }
   };
 
