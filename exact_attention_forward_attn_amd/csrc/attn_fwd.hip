@@ -106,6 +106,7 @@ struct KernelArgs {
   int hu;             // head units per batch entry: Hkv if packed, else Hq
   int pack;
   int n_mblk;         // query blocks per (batch entry, head unit)
+  int o_nt;           // store O with the non-temporal hint
   int nunit;          // B * hu
   int nsplit, split_len;
   int win_l, win_r;   // window widths (masked kernels; wide = unbounded)
@@ -713,7 +714,11 @@ void fwd_kernel(KernelArgs a) {
       if (qr < rows) {
         const int nr = pack ? gdiv(qr) : qr;
         const int hr = pack ? hu * grp + (qr - nr * grp) : hu;
-        *(u32x4*)((T*)a.o + (((int64_t)q_row0 + nr) * a.Hq + hr) * D + 8 * cc) = val;
+        u32x4* dst = (u32x4*)((T*)a.o + (((int64_t)q_row0 + nr) * a.Hq + hr) * D + 8 * cc);
+        if (a.o_nt)
+          __builtin_nontemporal_store(val, dst);
+        else
+          *dst = val;
       }
     }
   }
@@ -800,6 +805,12 @@ int launch(const FwdArgs& f, hipStream_t st) {
   a.hu = a.pack ? f.Hkv : f.H;
   const int rows = a.pack ? f.N * a.g : f.N;
   a.n_mblk = (rows + BM - 1) / BM;
+  // O is written once and not read again by this launch. For long
+  // sequences the non-temporal hint keeps it from displacing, in L2, the K/V
+  // tiles that a head's query blocks share (L2 fetches at d = 128, N = 8192:
+  // 1.29x -> 1.18x the Q/K/V bytes, same speed); for short ones the plain
+  // store measured as fast or faster, with the inputs cold in particular.
+  a.o_nt = f.N >= 2048 ? 1 : 0;
   a.nunit = f.B * a.hu;
   a.nsplit = f.nsplit > 1 ? f.nsplit : 1;
   a.split_len = f.nsplit > 1 ? f.split_len : 0x7fffffff;
