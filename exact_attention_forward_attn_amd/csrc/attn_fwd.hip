@@ -218,8 +218,8 @@ void fwd_kernel(KernelArgs a) {
   const int hq0 = pack ? hu * grp : hu;       // first query head of the unit
   const int64_t q_off = ((int64_t)q_row0 * a.Hq + hq0) * D;  // elements
   const int64_t k_off = ((int64_t)k_row0 * a.Hkv + hk) * D;
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc((const T*)a.q + q_off, (uint32_t)(len_q - 1) * RSQ + (uint32_t)(pack ? grp : 1) * D * 2);
+  const uint32_t qspan = (uint32_t)(len_q - 1) * RSQ + (uint32_t)(pack ? grp : 1) * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc((const T*)a.q + q_off, qspan);
   const uint32_t kspan = len_k > 0 ? (uint32_t)(len_k - 1) * RSK + D * 2 : 0;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc((const T*)a.k + k_off, kspan);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc((const T*)a.v + k_off, kspan);
@@ -706,6 +706,8 @@ void fwd_kernel(KernelArgs a) {
         const t4 ov = __builtin_convertvector(f, t4);
         *(u32x2*)(ow + rl * (2 * D) + (((4 * db + q4) ^ (rl & (CPR - 1))) << 4) + 8 * hl) = __builtin_bit_cast(u32x2, ov);
       }
+    // this unit's O rows, laid out like its Q rows (the non-temporal path)
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const T*)a.o + q_off, qspan);
 #pragma unroll
     for (int it = 0; it < 32 / RPI; ++it) {
       const int r = it * RPI + lane_e / CPR, cc = lane_e % CPR;
@@ -714,11 +716,14 @@ void fwd_kernel(KernelArgs a) {
       if (qr < rows) {
         const int nr = pack ? gdiv(qr) : qr;
         const int hr = pack ? hu * grp + (qr - nr * grp) : hu;
-        u32x4* dst = (u32x4*)((T*)a.o + (((int64_t)q_row0 + nr) * a.Hq + hr) * D + 8 * cc);
-        if (a.o_nt)
-          __builtin_nontemporal_store(val, dst);
-        else
-          *dst = val;
+        if (a.o_nt) {
+          // a buffer store, whose cache policy is an immediate (a plain
+          // store with the hint would be merged with the other branch)
+          const uint32_t ob = (uint32_t)nr * RSQ + (uint32_t)(hr - hq0) * (D * 2) + 16u * cc;
+          __builtin_amdgcn_raw_buffer_store_b128(val, ro, ob, 0, 2);
+        } else {
+          *(u32x4*)((T*)a.o + (((int64_t)q_row0 + nr) * a.Hq + hr) * D + 8 * cc) = val;
+        }
       }
     }
   }
@@ -809,7 +814,7 @@ int launch(const FwdArgs& f, hipStream_t st) {
   // sequences the non-temporal hint keeps it from displacing, in L2, the K/V
   // tiles that a head's query blocks share (L2 fetches at d = 128, N = 8192:
   // 1.29x -> 1.18x the Q/K/V bytes, same speed); for short ones the plain
-  // store measured as fast or faster, with the inputs cold in particular.
+  // store measured as fast or faster, with cold inputs in particular.
   a.o_nt = f.N >= 2048 ? 1 : 0;
   a.nunit = f.B * a.hu;
   a.nsplit = f.nsplit > 1 ? f.nsplit : 1;
