@@ -148,6 +148,20 @@ def test_varlen_mixed_lengths(gpu, causal, splits):
     _check(o, lse, o_ref, l_ref, (causal, splits))
 
 
+@pytest.mark.parametrize("pack", [0, 1])
+def test_long_rows_grouped_and_packed(gpu, pack):
+    """From 2048 rows on the tiled kernel stores O through a buffer resource
+    over each unit's rows (with the non-temporal hint): grouped heads with and
+    without head packing, in a dense batch and in a packed batch of unequal
+    lengths, causal and not, every row against the oracle."""
+    for causal in (False, True):
+        o, lse, o_ref, l_ref = _dense(gpu, 1, 2304, 2304, 8, 2, 128, causal, pack, 1, seed=21)
+        _check(o, lse, o_ref, l_ref, ("dense", pack, causal))
+        lens = np.array([2500, 700, 3000], dtype=np.int64)
+        o, lse, o_ref, l_ref = _varlen(gpu, lens, lens, 4, 2, 128, causal, 1, pack=pack, seed=22)
+        _check(o, lse, o_ref, l_ref, ("packed", pack, causal))
+
+
 @pytest.mark.parametrize("d", [64, 256])
 def test_varlen_equal_q_and_k_lengths(gpu, d):
     lens, _ = make_seqlens(5, 100, 400, seed=3)
