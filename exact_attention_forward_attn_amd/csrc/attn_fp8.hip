@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepKernelArgs a) {
     u32x2 w;
     w[0] = pack_e4m3(q[0], q[1], q[2], q[3]);
     w[1] = pack_e4m3(q[4], q[5], q[6], q[7]);
-    __builtin_amdgcn_raw_buffer_store_b64(w, rx8, n * (uint32_t)rs + 8 * li, 0, 0);
+    // non-temporal: the codes are read by a later launch, not from this L2
+    __builtin_amdgcn_raw_buffer_store_b64(w, rx8, n * (uint32_t)rs + 8 * li, 0, 2);
   }
 #endif
 }
