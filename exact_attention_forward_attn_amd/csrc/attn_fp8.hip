@@ -740,6 +740,9 @@ void fwd8_kernel(Fwd8Args a) {
     barrier();
     const int byte = wave * OW, slot = byte / G::TILE, within = byte - slot * G::TILE;
     char* ow = (slot == 0 ? kbuf0 : slot == 1 ? kbuf1 : slot == 2 ? vbuf0 : vbuf1) + within;
+    // O is written once (not read again by this launch): non-temporal, as a
+    // buffer store over this head's rows (the host keeps them under 2^31 B)
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + head_off, span * 2);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -756,7 +759,7 @@ void fwd8_kernel(Fwd8Args a) {
       const int r = it * RPI + lane / CPR, cc = lane % CPR;
       const u32x4 val = *(const u32x4*)(ow + r * (2 * D) + ((cc ^ (r & (CPR - 1))) << 4));
       const int qr = qw + r;
-      if (qr < N) *(u32x4*)(a.o + head_off + (int64_t)qr * a.H * D + 8 * cc) = val;
+      if (qr < N) __builtin_amdgcn_raw_buffer_store_b128(val, ro, ((uint32_t)qr * RS + 8 * cc) * 2, 0, 2);
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
