@@ -18,6 +18,7 @@ kernel source (null once the source changes).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--fp8] [--bwd] [--decode]
        python bench.py --copy-calibration   (plain copy kernel for PMC scaling)
        python bench.py --gemm-ceiling       (dense bf16 GEMM reference, torch.matmul)
+       python bench.py --fwd-only D N B H CAUSAL  (one 16-bit forward shape, for profiling)
        python bench.py --ingest-pmc DIR...  (rocprofv3 counter CSVs -> profiles/ summaries)
 """
 from __future__ import annotations
@@ -467,6 +468,8 @@ def main():
                     help="time only the backward at the headline shape (causal) and exit")
     ap.add_argument("--fp8-only", action="store_true",
                     help="time only the FP8 forward at the headline shape (128-row blocks + Hadamard) and exit")
+    ap.add_argument("--fwd-only", nargs=5, type=int, metavar=("D", "N", "B", "H", "CAUSAL"),
+                    help="time only the 16-bit forward at one shape (for profiling) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--out", default=None, help="write all measurements to this JSON file")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -510,6 +513,13 @@ def main():
         h = HEADLINE
         r = bench_bwd(ea, h["B"], h["N"], h["H"], h["d"], True, args.steps, args.warmup)
         print(json.dumps({"bwd": r}), flush=True)
+        return
+
+    if args.fwd_only:
+        d, N, B, H, causal = args.fwd_only
+        r = bench_bf16(ea, B, N, H, d, bool(causal), args.steps, args.warmup)
+        r.pop("_out", None)
+        print(json.dumps({"fwd": r}), flush=True)
         return
 
     if args.decode_only:
